@@ -1,0 +1,309 @@
+/*
+ * lqmm oracle: plain, slow, double-precision CPU reference for the
+ * block-quantized matmul hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may call, link or
+ * load this file or the library built from it; only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg use it. It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * What it computes (the plain definition, in IEEE double):
+ *   1. decode every fp16 field from its raw bits;
+ *   2. dequantize every weight to a real number with the block format's
+ *      value formula;
+ *   3. multiply the dense dequantized matrix with the activations.
+ * The method being checked is the quantization-aware matmul of
+ * "Resumo Tecnico: Llamas na Web", section "Design de Shader Consciente de
+ * Quantizacao": quantized blocks are dequantized (in registers for the decode
+ * mat-vec, in shared memory for the prefill matmul) and multiplied. Whatever
+ * order a kernel dequantizes and accumulates in, the exact result is this
+ * dequantize-then-multiply product, which the oracle computes with only
+ * summation rounding (relative error about K * 2^-53).
+ *
+ * The fp32 tiled GEMM follows "Compute Shaders con WebGPU para Inferencia ML",
+ * section "El Nucleo: Multiplicacion de Matrices en WGSL": C = A * B on
+ * row-major M x K and K x N matrices, any M, N, K; its zero-padded edge tiles
+ * add nothing, so the plain triple sum is the definition.
+ *
+ * Block byte layouts (llama.cpp / GGUF style; the pages name these formats but
+ * do not print their bytes, so this reading is stated here once):
+ *   Q4_0, 18 bytes per 32 weights: bytes 0-1 fp16 d (little endian),
+ *     bytes 2-17 qs[16]; weight j (0<=j<16) is the low nibble of qs[j],
+ *     weight j+16 the high nibble; w = d * (q - 8), q in 0..15.
+ *   Q8_0, 34 bytes per 32 weights: bytes 0-1 fp16 d, bytes 2-33 int8 q[32]
+ *     (two's complement); w = d * q.
+ *   Q4_K, 144 bytes per 256 weights: bytes 0-1 fp16 d, 2-3 fp16 dmin,
+ *     4-15 scales[12], 16-143 qs[128]. Sub-block s (weights 32s..32s+31) has a
+ *     6-bit scale sc_s and 6-bit min m_s:
+ *       s < 4 : sc_s = scales[s] & 63,  m_s = scales[s+4] & 63
+ *       s >= 4: sc_s = (scales[s+4] & 15) | ((scales[s-4] >> 6) << 4)
+ *               m_s  = (scales[s+4] >> 4) | ((scales[s]   >> 6) << 4)
+ *     weight l of sub-block s has q = nibble of qs[32*(s/2) + l], low nibble
+ *     for even s, high nibble for odd s; w = d * sc_s * q - dmin * m_s.
+ * A weight matrix of N output rows and K inputs stores row n as K/32 (or
+ * K/256) consecutive blocks; rows are consecutive with no padding.
+ *
+ * Test hooks: LQMM_ORACLE_MUTANT selects a deliberately wrong variant of one
+ * step. It is 0 in every normal build and is only set by the test that checks
+ * that the pins catch such mistakes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef LQMM_ORACLE_MUTANT
+#define LQMM_ORACLE_MUTANT 0
+#endif
+
+#define QK 32    /* weights per Q4_0 / Q8_0 block */
+#define QKK 256  /* weights per Q4_K super-block */
+
+/* IEEE 754 binary16 -> double, from the format's definition: sign bit,
+ * 5-bit biased exponent (bias 15), 10-bit fraction; exponent 0 encodes zero
+ * and subnormals (fraction * 2^-24), exponent 31 encodes inf / NaN. */
+double lqmm_oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0) {
+#if LQMM_ORACLE_MUTANT == 7
+    v = ldexp((double)(1024 + f), -25); /* subnormal treated as normal */
+#else
+    v = ldexp((double)f, -24);
+#endif
+  } else if (e == 31) {
+    v = f ? NAN : INFINITY;
+  } else {
+#if LQMM_ORACLE_MUTANT == 8
+    v = ldexp((double)(1024 + f), e - 24); /* exponent bias off by one */
+#else
+    v = ldexp((double)(1024 + f), e - 25);
+#endif
+  }
+  return sign ? -v : v;
+}
+
+/* Element-wise decode of n fp16 bit patterns. */
+void lqmm_oracle_f16_array_to_f64(const uint16_t *h, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = lqmm_oracle_f16_to_f64(h[i]);
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Dequantize one Q4_0 block (18 bytes) into 32 doubles: w = d * (q - 8). */
+static void deq_q4_0_block(const uint8_t *blk, double *w) {
+  double d = lqmm_oracle_f16_to_f64(rd16(blk));
+  const uint8_t *qs = blk + 2;
+  for (int j = 0; j < 16; ++j) {
+    int lo = qs[j] & 15, hi = qs[j] >> 4;
+#if LQMM_ORACLE_MUTANT == 1
+    /* sequential nibble order (weight 2j low, 2j+1 high) */
+    w[2 * j] = d * (lo - 8);
+    w[2 * j + 1] = d * (hi - 8);
+#elif LQMM_ORACLE_MUTANT == 2
+    w[j] = d * lo; /* offset 8 dropped */
+    w[j + 16] = d * hi;
+#else
+    w[j] = d * (lo - 8);
+    w[j + 16] = d * (hi - 8);
+#endif
+  }
+}
+
+/* Dequantize one Q8_0 block (34 bytes) into 32 doubles: w = d * q. */
+static void deq_q8_0_block(const uint8_t *blk, double *w) {
+  double d = lqmm_oracle_f16_to_f64(rd16(blk));
+  for (int j = 0; j < QK; ++j) {
+#if LQMM_ORACLE_MUTANT == 6
+    int q = blk[2 + j]; /* read as unsigned */
+#else
+    int q = (int8_t)blk[2 + j];
+#endif
+    w[j] = d * q;
+  }
+}
+
+/* The 6-bit scale and min of sub-block s of a Q4_K super-block. */
+static void q4_k_scale_min(const uint8_t *scales, int s, int *sc, int *m) {
+  if (s < 4) {
+    *sc = scales[s] & 63;
+    *m = scales[s + 4] & 63;
+  } else {
+#if LQMM_ORACLE_MUTANT == 3
+    *sc = scales[s + 4] & 15; /* high two bits of sc dropped */
+#else
+    *sc = (scales[s + 4] & 15) | ((scales[s - 4] >> 6) << 4);
+#endif
+    *m = (scales[s + 4] >> 4) | ((scales[s] >> 6) << 4);
+  }
+}
+
+/* Dequantize one Q4_K super-block (144 bytes) into 256 doubles:
+ * w = d * sc_s * q - dmin * m_s. */
+static void deq_q4_k_block(const uint8_t *blk, double *w) {
+  double d = lqmm_oracle_f16_to_f64(rd16(blk));
+  double dmin = lqmm_oracle_f16_to_f64(rd16(blk + 2));
+  const uint8_t *scales = blk + 4;
+  const uint8_t *qs = blk + 16;
+  for (int s = 0; s < 8; ++s) {
+    int sc, m;
+    q4_k_scale_min(scales, s, &sc, &m);
+    for (int l = 0; l < 32; ++l) {
+      uint8_t byte = qs[32 * (s / 2) + l];
+#if LQMM_ORACLE_MUTANT == 5
+      int q = (s % 2 == 0) ? (byte >> 4) : (byte & 15); /* halves swapped */
+#else
+      int q = (s % 2 == 0) ? (byte & 15) : (byte >> 4);
+#endif
+#if LQMM_ORACLE_MUTANT == 4
+      w[32 * s + l] = d * sc * q + dmin * m; /* min term sign flipped */
+#else
+      w[32 * s + l] = d * sc * q - dmin * m;
+#endif
+    }
+  }
+}
+
+/* ---- dense dequantization of whole rows (exposed for the pins) ---- */
+
+void lqmm_oracle_dequant_q4_0(const uint8_t *W, int64_t N, int64_t K, double *out) {
+  int64_t nb = K / QK;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < nb; ++b)
+      deq_q4_0_block(W + (n * nb + b) * 18, out + n * K + b * QK);
+}
+
+void lqmm_oracle_dequant_q8_0(const uint8_t *W, int64_t N, int64_t K, double *out) {
+  int64_t nb = K / QK;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < nb; ++b)
+      deq_q8_0_block(W + (n * nb + b) * 34, out + n * K + b * QK);
+}
+
+void lqmm_oracle_dequant_q4_k(const uint8_t *W, int64_t N, int64_t K, double *out) {
+  int64_t nb = K / QKK;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < nb; ++b)
+      deq_q4_k_block(W + (n * nb + b) * 144, out + n * K + b * QKK);
+}
+
+/* ---- GEMV: y[b][n] = sum_k W[n][k] * x[b][k] ----
+ * Weight-matrix times activation for decode (one or a few tokens), the
+ * mat-vec case of "Llamas na Web", "Design de Shader Consciente de
+ * Quantizacao". x is batch x K fp32 row-major; y is batch x N double.
+ * rows/nrows select the output rows to compute (rows == NULL: all N, and
+ * nrows is ignored); y is then batch x nrows in the order given. */
+typedef void (*deq_row_fn)(const uint8_t *W, int64_t n, int64_t K, double *w);
+
+static void row_q4_0(const uint8_t *W, int64_t n, int64_t K, double *w) {
+  int64_t nb = K / QK;
+  for (int64_t b = 0; b < nb; ++b) deq_q4_0_block(W + (n * nb + b) * 18, w + b * QK);
+}
+static void row_q8_0(const uint8_t *W, int64_t n, int64_t K, double *w) {
+  int64_t nb = K / QK;
+  for (int64_t b = 0; b < nb; ++b) deq_q8_0_block(W + (n * nb + b) * 34, w + b * QK);
+}
+static void row_q4_k(const uint8_t *W, int64_t n, int64_t K, double *w) {
+  int64_t nb = K / QKK;
+  for (int64_t b = 0; b < nb; ++b) deq_q4_k_block(W + (n * nb + b) * 144, w + b * QKK);
+}
+
+static void gemv_generic(deq_row_fn deq, const uint8_t *W, const float *x, double *y,
+                         int64_t N, int64_t K, int64_t batch, const int64_t *rows,
+                         int64_t nrows) {
+  int64_t R = rows ? nrows : N;
+#pragma omp parallel
+  {
+    double *w = (double *)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < R; ++i) {
+      int64_t n = rows ? rows[i] : i;
+      deq(W, n, K, w);
+      for (int64_t b = 0; b < batch; ++b) {
+        const float *xb = x + b * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += w[k] * (double)xb[k];
+        y[b * R + i] = acc;
+      }
+    }
+    free(w);
+  }
+}
+
+void lqmm_oracle_gemv_q4_0(const uint8_t *W, const float *x, double *y, int64_t N,
+                           int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
+  gemv_generic(row_q4_0, W, x, y, N, K, batch, rows, nrows);
+}
+
+void lqmm_oracle_gemv_q4_k(const uint8_t *W, const float *x, double *y, int64_t N,
+                           int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
+  gemv_generic(row_q4_k, W, x, y, N, K, batch, rows, nrows);
+}
+
+/* ---- Q8_0 x fp16 GEMM: Y[m][n] = sum_k X[m][k] * W[n][k] ----
+ * The prefill matmul of "Llamas na Web", "Design de Shader Consciente de
+ * Quantizacao" (blocks loaded, dequantized and reused). X is M x K raw fp16
+ * bits, row-major; Y is M x N double (the unrounded product). cols/ncols
+ * select output columns n (cols == NULL: all N); Y is then M x ncols. */
+void lqmm_oracle_gemm_q8_0_f16(const uint8_t *W, const uint16_t *X, double *Y, int64_t M,
+                               int64_t N, int64_t K, const int64_t *cols, int64_t ncols) {
+  int64_t C = cols ? ncols : N;
+  double *Xd = (double *)malloc(sizeof(double) * (size_t)(M * K));
+  for (int64_t i = 0; i < M * K; ++i) Xd[i] = lqmm_oracle_f16_to_f64(X[i]);
+#pragma omp parallel
+  {
+    double *w = (double *)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int64_t j = 0; j < C; ++j) {
+      int64_t n = cols ? cols[j] : j;
+      row_q8_0(W, n, K, w);
+      for (int64_t m = 0; m < M; ++m) {
+        const double *xm = Xd + m * K;
+        double acc = 0.0;
+#if LQMM_ORACLE_MUTANT == 10
+        for (int64_t k = 0; k < K; ++k) acc += xm[k] * w[(k * 7) % K]; /* k index scrambled */
+#else
+        for (int64_t k = 0; k < K; ++k) acc += xm[k] * w[k];
+#endif
+        Y[m * C + j] = acc;
+      }
+    }
+    free(w);
+  }
+  free(Xd);
+}
+
+/* ---- fp32 GEMM: C[i][j] = sum_k A[i][k] * B[k][j] ----
+ * "Compute Shaders con WebGPU para Inferencia ML", "El Nucleo: Multiplicacion
+ * de Matrices en WGSL". A is M x K, B is K x N, both fp32 row-major; C is
+ * M x N double. rows/nrows select output rows i (rows == NULL: all M). */
+void lqmm_oracle_sgemm(const float *A, const float *B, double *C, int64_t M, int64_t N,
+                       int64_t K, const int64_t *rows, int64_t nrows) {
+  int64_t R = rows ? nrows : M;
+  /* column j of B, gathered once so the inner sum walks contiguous memory */
+  double *Bt = (double *)malloc(sizeof(double) * (size_t)(N * K));
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < N; ++j)
+#if LQMM_ORACLE_MUTANT == 9
+      Bt[j * K + k] = (double)B[(j % K) * N + (k % N)]; /* B read transposed */
+#else
+      Bt[j * K + k] = (double)B[k * N + j];
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t i = rows ? rows[r] : r;
+    const float *a = A + i * K;
+    for (int64_t j = 0; j < N; ++j) {
+      const double *b = Bt + j * K;
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += (double)a[k] * b[k];
+      C[r * N + j] = acc;
+    }
+  }
+  free(Bt);
+}
+
+/* Mutant id this library was built with (0 = the real oracle). */
+int lqmm_oracle_mutant(void) { return LQMM_ORACLE_MUTANT; }

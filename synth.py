@@ -1,0 +1,227 @@
+"""Seeded synthetic inputs for the block-quantized matmul hot path.
+
+This module is shared by the tests, the benchmark and the smoke check. It
+holds the random draws and the byte packing of the block formats, and none of
+the arithmetic being checked: it never dequantizes a weight and never
+multiplies anything. Both the HIP library and the CPU oracle read the bytes it
+produces.
+
+Workloads: synthetic Llama-shaped layers with the value distributions of the
+benchmark configurations (the pages measure whole models whose weights are not
+available; these seeded layers stand in for them):
+
+* Q4_0 decode GEMV: fp16 scale d = |N(0,1)| * 0.02, codes q ~ U{0..15},
+  x ~ N(0,1) fp32.
+* Q8_0 x fp16 prefill GEMM: d = |N(0,1)| * 0.01, q ~ U{-127..127},
+  X ~ N(0,1) rounded to fp16.
+* Q4_K decode GEMV: d, dmin = |N(0,1)| * 0.01, 6-bit sc, m ~ U{0..63},
+  q ~ U{0..15}, x ~ N(0,1) fp32.
+* fp32 GEMM: A, B ~ U(-1, 1).
+
+Every case draws from ``numpy.random.default_rng(seed)`` in the order: scales
+(d, then dmin), codes (q, then sc, m), activations. fp16 values are rounded
+from float64 with IEEE round-to-nearest-even (``astype(np.float16)``).
+
+Byte layouts (llama.cpp / GGUF style; the pages name the formats, not their
+bytes): see ``pack_q4_0``, ``pack_q8_0`` and ``pack_q4_k``.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+Q4_0_BYTES = 18   # per 32 weights
+Q8_0_BYTES = 34   # per 32 weights
+Q4_K_BYTES = 144  # per 256 weights
+
+
+def _f16_bytes(a: np.ndarray) -> np.ndarray:
+    """Little-endian bytes of an fp16 array, shape (..., 2)."""
+    return np.ascontiguousarray(a.astype("<f2")).view(np.uint8).reshape(a.shape + (2,))
+
+
+def pack_q4_0(d: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q4_0 blocks.
+
+    d: (N, K/32) float16 scales. q: (N, K) codes in 0..15.
+    Block = [d (2 bytes LE)][qs[16]]; weight j of the block sits in the low
+    nibble of qs[j] for j < 16 and in the high nibble of qs[j-16] otherwise.
+    Returns (N, K/32*18) uint8.
+    """
+    N, K = q.shape
+    nb = K // 32
+    qb = q.astype(np.uint8).reshape(N, nb, 32)
+    qs = (qb[..., :16] & 0xF) | ((qb[..., 16:] & 0xF) << 4)
+    blk = np.concatenate([_f16_bytes(d.reshape(N, nb)), qs], axis=-1)
+    return np.ascontiguousarray(blk.reshape(N, nb * Q4_0_BYTES))
+
+
+def pack_q8_0(d: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack Q8_0 blocks: [d (2 bytes LE)][q[32] as two's-complement int8].
+
+    d: (N, K/32) float16. q: (N, K) int8. Returns (N, K/32*34) uint8.
+    """
+    N, K = q.shape
+    nb = K // 32
+    qb = q.astype(np.int8).view(np.uint8).reshape(N, nb, 32)
+    blk = np.concatenate([_f16_bytes(d.reshape(N, nb)), qb], axis=-1)
+    return np.ascontiguousarray(blk.reshape(N, nb * Q8_0_BYTES))
+
+
+def pack_q4_k_scales(sc: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """Pack eight 6-bit (sc, m) pairs into the 12 scale bytes of a Q4_K block.
+
+    Bytes 0-3: sc[0..3] in bits 0-5, bits 4-5 of sc[4..7] in bits 6-7.
+    Bytes 4-7: m[0..3] in bits 0-5, bits 4-5 of m[4..7] in bits 6-7.
+    Bytes 8-11: bits 0-3 of sc[4..7] (low nibble), bits 0-3 of m[4..7]
+    (high nibble). sc, m: (..., 8) integers in 0..63. Returns (..., 12) uint8.
+    """
+    sc = sc.astype(np.uint8)
+    m = m.astype(np.uint8)
+    b0 = (sc[..., 0:4] & 63) | ((sc[..., 4:8] >> 4) << 6)
+    b1 = (m[..., 0:4] & 63) | ((m[..., 4:8] >> 4) << 6)
+    b2 = (sc[..., 4:8] & 15) | ((m[..., 4:8] & 15) << 4)
+    return np.concatenate([b0, b1, b2], axis=-1).astype(np.uint8)
+
+
+def pack_q4_k(d, dmin, sc, m, q) -> np.ndarray:
+    """Pack Q4_K super-blocks of 256 weights (144 bytes each).
+
+    Layout: [d (2)][dmin (2)][scales (12)][qs (128)]. Sub-block s holds
+    weights 32s..32s+31; its codes are the low nibbles (even s) or high
+    nibbles (odd s) of qs[32*(s//2) .. 32*(s//2)+31].
+    d, dmin: (N, K/256) float16; sc, m: (N, K/256, 8) in 0..63;
+    q: (N, K) in 0..15. Returns (N, K/256*144) uint8.
+    """
+    N, K = q.shape
+    nsb = K // 256
+    qb = q.astype(np.uint8).reshape(N, nsb, 4, 2, 32)
+    qs = ((qb[:, :, :, 0, :] & 0xF) | ((qb[:, :, :, 1, :] & 0xF) << 4)).reshape(N, nsb, 128)
+    blk = np.concatenate(
+        [_f16_bytes(d.reshape(N, nsb)), _f16_bytes(dmin.reshape(N, nsb)),
+         pack_q4_k_scales(sc.reshape(N, nsb, 8), m.reshape(N, nsb, 8)), qs],
+        axis=-1)
+    return np.ascontiguousarray(blk.reshape(N, nsb * Q4_K_BYTES))
+
+
+def _half_normal_f16(rng, shape, scale):
+    return (np.abs(rng.standard_normal(shape)) * scale).astype(np.float16)
+
+
+@dataclasses.dataclass
+class Q4_0Case:
+    W: np.ndarray      # (N, K/32*18) uint8
+    x: np.ndarray      # (batch, K) float32
+    d: np.ndarray      # (N, K/32) float16
+    q: np.ndarray      # (N, K) uint8
+    N: int
+    K: int
+    batch: int
+
+
+@dataclasses.dataclass
+class Q4_KCase:
+    W: np.ndarray      # (N, K/256*144) uint8
+    x: np.ndarray      # (batch, K) float32
+    d: np.ndarray
+    dmin: np.ndarray
+    sc: np.ndarray     # (N, K/256, 8)
+    m: np.ndarray      # (N, K/256, 8)
+    q: np.ndarray      # (N, K)
+    N: int
+    K: int
+    batch: int
+
+
+@dataclasses.dataclass
+class Q8_0Case:
+    W: np.ndarray      # (N, K/32*34) uint8
+    X: np.ndarray      # (M, K) float16
+    d: np.ndarray
+    q: np.ndarray      # (N, K) int8
+    M: int
+    N: int
+    K: int
+
+
+@dataclasses.dataclass
+class SgemmCase:
+    A: np.ndarray      # (M, K) float32
+    B: np.ndarray      # (K, N) float32
+    M: int
+    N: int
+    K: int
+
+
+def q4_0_case(N: int, K: int, batch: int = 1, seed: int = 0, scale: float = 0.02) -> Q4_0Case:
+    assert K % 32 == 0
+    rng = np.random.default_rng(seed)
+    d = _half_normal_f16(rng, (N, K // 32), scale)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    x = rng.standard_normal((batch, K)).astype(np.float32)
+    return Q4_0Case(pack_q4_0(d, q), x, d, q, N, K, batch)
+
+
+def q4_k_case(N: int, K: int, batch: int = 1, seed: int = 0, scale: float = 0.01) -> Q4_KCase:
+    assert K % 256 == 0
+    rng = np.random.default_rng(seed)
+    nsb = K // 256
+    d = _half_normal_f16(rng, (N, nsb), scale)
+    dmin = _half_normal_f16(rng, (N, nsb), scale)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(N, nsb, 8), dtype=np.uint8)
+    m = rng.integers(0, 64, size=(N, nsb, 8), dtype=np.uint8)
+    x = rng.standard_normal((batch, K)).astype(np.float32)
+    return Q4_KCase(pack_q4_k(d, dmin, sc, m, q), x, d, dmin, sc, m, q, N, K, batch)
+
+
+def q8_0_case(M: int, N: int, K: int, seed: int = 0, scale: float = 0.01) -> Q8_0Case:
+    assert K % 32 == 0
+    rng = np.random.default_rng(seed)
+    d = _half_normal_f16(rng, (N, K // 32), scale)
+    q = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    return Q8_0Case(pack_q8_0(d, q), X, d, q, M, N, K)
+
+
+def sgemm_case(M: int, N: int, K: int, seed: int = 0) -> SgemmCase:
+    rng = np.random.default_rng(seed)
+    A = rng.uniform(-1.0, 1.0, (M, K)).astype(np.float32)
+    B = rng.uniform(-1.0, 1.0, (K, N)).astype(np.float32)
+    return SgemmCase(A, B, M, N, K)
+
+
+# The benchmark configurations, by what they are.
+CONFIGS = {
+    # Q4_0 GEMV, 1024 out x 1024 in, batch 1, seed 0 (the small parity case)
+    "q4_0_gemv_1024": dict(kind="q4_0", N=1024, K=1024, batch=1),
+    # dense fp32 tiled GEMM, M = N = K = 2048
+    "sgemm_2048": dict(kind="sgemm", M=2048, N=2048, K=2048),
+    # Q4_0 decode GEMV at 7B-layer shapes, K = 4096
+    "q4_0_gemv_4096x4096_b1": dict(kind="q4_0", N=4096, K=4096, batch=1),
+    "q4_0_gemv_4096x4096_b4": dict(kind="q4_0", N=4096, K=4096, batch=4),
+    "q4_0_gemv_11008x4096_b1": dict(kind="q4_0", N=11008, K=4096, batch=1),
+    "q4_0_gemv_11008x4096_b4": dict(kind="q4_0", N=11008, K=4096, batch=4),
+    "q4_0_gemv_12288x4096_b1": dict(kind="q4_0", N=12288, K=4096, batch=1),
+    "q4_0_gemv_12288x4096_b4": dict(kind="q4_0", N=12288, K=4096, batch=4),
+    # Q8_0 x fp16 prefill GEMM, 512 tokens, N = 14336, K = 4096
+    "q8_0_gemm_512x14336x4096": dict(kind="q8_0", M=512, N=14336, K=4096),
+    # Q4_K GEMV at a 70B FFN shape, K = 8192, N = 28672
+    "q4_k_gemv_28672x8192_b1": dict(kind="q4_k", N=28672, K=8192, batch=1),
+    "q4_k_gemv_28672x8192_b8": dict(kind="q4_k", N=28672, K=8192, batch=8),
+}
+
+
+def make(name: str, seed: int = 0):
+    c = dict(CONFIGS[name])
+    kind = c.pop("kind")
+    if kind == "q4_0":
+        return q4_0_case(c["N"], c["K"], c["batch"], seed)
+    if kind == "q4_k":
+        return q4_k_case(c["N"], c["K"], c["batch"], seed)
+    if kind == "q8_0":
+        return q8_0_case(c["M"], c["N"], c["K"], seed)
+    if kind == "sgemm":
+        return sgemm_case(c["M"], c["N"], c["K"], seed)
+    raise KeyError(name)

@@ -1,0 +1,325 @@
+"""Pins for the CPU oracle: checks against facts other than the oracle itself.
+
+Each pin is a function of an ``oracle.Oracle`` instance that raises
+AssertionError on a mismatch. ``test_oracle_pins.py`` runs them against the
+real oracle; ``test_oracle_mutants.py`` runs them against oracles with a
+planted mistake and requires that some pin fails for every mistake.
+
+Kinds of pin (none of them re-types the oracle's own code):
+* library routine: numpy's IEEE fp16 decoding, numpy float64 matmul;
+* hand-worked blocks from ``tests/golden`` (constructed, with derivations);
+* closed forms and invariants (x = ones, one-hot x, linearity, batching);
+* round trip: requantizing the oracle's dequantized weights with the block's
+  own scales must give back the generator's integer codes;
+* brute force: exact rational sums (``fractions.Fraction``) on tiny shapes.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = (s.strip() for s in line.split("=", 1))
+            out[k] = v
+    return out
+
+
+def _hex(s: str) -> np.ndarray:
+    return np.frombuffer(bytes.fromhex(s), dtype=np.uint8).copy()
+
+
+def _onehot(K, k):
+    x = np.zeros((1, K), np.float32)
+    x[0, k] = 1.0
+    return x
+
+
+# ---------------------------------------------------------------- fp16 decode
+def pin_f16_exhaustive(o):
+    """All 65,536 binary16 patterns decode exactly as numpy's float16."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zero is kept
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+# --------------------------------------------------------------- hand-worked
+def pin_q4_0_worked(o):
+    g = read_golden("q4_0_block.txt")
+    W = _hex(g["block_hex"])
+    K = 32
+    cases = {"ones": np.ones((1, K), np.float32), "e1": _onehot(K, 1),
+             "e16": _onehot(K, 16), "e31": _onehot(K, 31),
+             "ramp": np.arange(K, dtype=np.float32)[None]}
+    for key, x in cases.items():
+        y = o.gemv_q4_0(W, x, 1, K)
+        assert y[0, 0] == float(g[key]), (key, y[0, 0])
+        yh = o.gemv_q4_0(_hex(g["d_half_block_hex"]), x, 1, K)
+        assert yh[0, 0] == float(g[key]) / 2, (key, yh[0, 0])
+
+
+def pin_q8_0_worked(o):
+    g = read_golden("q8_0_block.txt")
+    K = 32
+    for blk, keys in (("a", {"ones": None, "e0": 0, "e31": 31}),
+                      ("b", {"ones": None, "e0": 0, "e1": 1})):
+        W = _hex(g[f"{blk}_hex"])
+        for key, k in keys.items():
+            X = np.ones((1, K), np.float16) if k is None else _onehot(K, k).astype(np.float16)
+            Y = o.gemm_q8_0_f16(W, X, 1, K)
+            assert Y[0, 0] == float(g[f"{blk}_{key}"]), (blk, key, Y[0, 0])
+
+
+def pin_q4_k_worked(o):
+    g = read_golden("q4_k_block.txt")
+    K = 256
+    head = _hex("003c0038" + g["scales_hex"])
+    qa = np.full(128, 0x11, np.uint8)
+    i = np.arange(128)
+    qb = ((i % 16) | ((15 - i % 16) << 4)).astype(np.uint8)
+    Wa = np.concatenate([head, qa])
+    Wb = np.concatenate([head, qb])
+    ones = np.ones((1, K), np.float32)
+    assert o.gemv_q4_k(Wa, ones, 1, K)[0, 0] == float(g["a_ones"])
+    assert o.gemv_q4_k(Wa, _onehot(K, 167), 1, K)[0, 0] == float(g["a_e167"])
+    assert o.gemv_q4_k(Wa, _onehot(K, 128), 1, K)[0, 0] == float(g["a_e128"])
+    assert o.gemv_q4_k(Wb, ones, 1, K)[0, 0] == float(g["b_ones"])
+    for k in (3, 35, 180, 223):
+        assert o.gemv_q4_k(Wb, _onehot(K, k), 1, K)[0, 0] == float(g[f"b_e{k}"]), k
+
+
+def pin_packers_match_golden(o):
+    """The generator's packers reproduce the hand-worked bytes (so the
+    round-trip pins below test the oracle against the stated layout)."""
+    g = read_golden("q4_0_block.txt")
+    j = np.arange(16)
+    q = np.concatenate([j, 15 - j]).astype(np.uint8)[None]
+    got = synth.pack_q4_0(np.array([[1.0]], np.float16), q)
+    assert got.tobytes().hex() == g["block_hex"]
+    g8 = read_golden("q8_0_block.txt")
+    q8 = (np.arange(32) - 16).astype(np.int8)[None]
+    assert synth.pack_q8_0(np.array([[0.25]], np.float16), q8).tobytes().hex() == g8["a_hex"]
+    gk = read_golden("q4_k_block.txt")
+    sc = np.array([[1, 2, 3, 4, 63, 33, 17, 48]], np.uint8)
+    m = np.array([[0, 1, 2, 3, 63, 40, 5, 32]], np.uint8)
+    assert synth.pack_q4_k_scales(sc, m).tobytes().hex() == gk["scales_hex"]
+    qk = np.ones((1, 256), np.uint8)
+    blk = synth.pack_q4_k(np.array([[1.0]], np.float16), np.array([[0.5]], np.float16),
+                          sc[None], m[None], qk)
+    assert blk.tobytes().hex() == "003c0038" + gk["scales_hex"] + "11" * 128
+
+
+# ---------------------------------------------------------------- round trip
+def pin_round_trip(o):
+    """Requantize the oracle's dequantized weights with each block's own
+    scale(s): the generator's integer codes come back exactly."""
+    c = synth.q4_0_case(37, 256, seed=3)
+    w = o.dequant_q4_0(c.W, c.N, c.K)
+    d = c.d.astype(np.float64).repeat(32, axis=1)
+    nz = d != 0
+    assert np.array_equal(w[nz] / d[nz] + 8, c.q.astype(np.float64)[nz])
+    assert np.all(w[~nz] == 0)
+
+    c8 = synth.q8_0_case(1, 29, 320, seed=4)
+    w8 = o.dequant_q8_0(c8.W, c8.N, c8.K)
+    d8 = c8.d.astype(np.float64).repeat(32, axis=1)
+    nz = d8 != 0
+    assert np.array_equal(w8[nz] / d8[nz], c8.q.astype(np.float64)[nz])
+
+    ck = synth.q4_k_case(23, 512, seed=5)
+    wk = o.dequant_q4_k(ck.W, ck.N, ck.K)
+    N, nsb = ck.N, ck.K // 256
+    dd = np.repeat(ck.d.astype(np.float64), 256, axis=1)
+    dm = np.repeat(ck.dmin.astype(np.float64), 256, axis=1)
+    sc = np.repeat(ck.sc.reshape(N, nsb * 8).astype(np.float64), 32, axis=1)
+    mm = np.repeat(ck.m.reshape(N, nsb * 8).astype(np.float64), 32, axis=1)
+    ok = (dd * sc) != 0
+    qrec = (wk[ok] + dm[ok] * mm[ok]) / (dd[ok] * sc[ok])
+    assert np.allclose(qrec, ck.q.astype(np.float64)[ok], rtol=0, atol=1e-9)
+    assert np.array_equal(np.rint(qrec), ck.q.astype(np.float64)[ok])
+    # where sc = 0 the weight is -dmin * m whatever q is
+    z = ~ok & (dd != 0)
+    assert np.array_equal(wk[z], -(dm[z] * mm[z]))
+
+
+# --------------------------------------------------- closed forms, invariants
+def pin_closed_forms_q4_0(o):
+    c = synth.q4_0_case(19, 192, seed=7)
+    N, K = c.N, c.K
+    ones = np.ones((1, K), np.float32)
+    y = o.gemv_q4_0(c.W, ones, N, K)[0]
+    # x = ones: y_n = sum over blocks of d * (sum q - 256)
+    qs = c.q.reshape(N, K // 32, 32).astype(np.int64).sum(-1) - 256
+    ref = (c.d.astype(np.float64) * qs).sum(-1)
+    assert np.allclose(y, ref, rtol=1e-13, atol=0)
+    # one-hot x extracts a column exactly
+    for k in (0, 15, 16, 31, 100, 191):
+        col = o.gemv_q4_0(c.W, _onehot(K, k), N, K)[0]
+        ref = c.d[:, k // 32].astype(np.float64) * (c.q[:, k].astype(np.float64) - 8)
+        assert np.array_equal(col, ref), k
+    # linearity and batch independence
+    rng = np.random.default_rng(11)
+    xa = rng.standard_normal((1, K)).astype(np.float32)
+    xb = rng.standard_normal((1, K)).astype(np.float32)
+    ya, yb = o.gemv_q4_0(c.W, xa, N, K), o.gemv_q4_0(c.W, xb, N, K)
+    ysum = o.gemv_q4_0(c.W, (xa.astype(np.float64) + xb).astype(np.float32), N, K)
+    assert np.allclose(ysum, ya + yb, rtol=1e-6, atol=1e-6)  # x rounding to fp32 only
+    yab = o.gemv_q4_0(c.W, np.concatenate([xa, xb]), N, K)
+    assert np.array_equal(yab[0], ya[0]) and np.array_equal(yab[1], yb[0])
+    # a row subset returns the same rows
+    rows = [18, 0, 5]
+    assert np.array_equal(o.gemv_q4_0(c.W, xa, N, K, rows=rows)[0], ya[0, rows])
+
+
+def pin_closed_forms_q4_k(o):
+    ck = synth.q4_k_case(11, 512, seed=8)
+    N, K = ck.N, ck.K
+    nsb = K // 256
+    ones = np.ones((1, K), np.float32)
+    y = o.gemv_q4_k(ck.W, ones, N, K)[0]
+    qsum = ck.q.reshape(N, nsb, 8, 32).astype(np.int64).sum(-1)
+    ref = (ck.d.astype(np.float64)[..., None] * ck.sc * qsum
+           - 32 * ck.dmin.astype(np.float64)[..., None] * ck.m).sum((-1, -2))
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+    for k in (0, 31, 32, 63, 255, 256 + 77, 511):
+        col = o.gemv_q4_k(ck.W, _onehot(K, k), N, K)[0]
+        sb, s = k // 256, (k % 256) // 32
+        ref = (ck.d[:, sb].astype(np.float64) * ck.sc[:, sb, s] * ck.q[:, k]
+               - ck.dmin[:, sb].astype(np.float64) * ck.m[:, sb, s])
+        assert np.array_equal(col, ref), k
+
+
+def pin_closed_forms_gemm(o):
+    c = synth.q8_0_case(5, 13, 96, seed=9)
+    X1 = np.ones((1, c.K), np.float16)
+    Y = o.gemm_q8_0_f16(c.W, X1, c.N, c.K)[0]
+    ref = (c.d.astype(np.float64) * c.q.reshape(c.N, -1, 32).astype(np.int64).sum(-1)).sum(-1)
+    assert np.allclose(Y, ref, rtol=1e-13, atol=0)
+    # one-hot row of X extracts column k of W (row n of the weight matrix)
+    Xe = np.zeros((1, c.K), np.float16)
+    Xe[0, 40] = 1
+    col = o.gemm_q8_0_f16(c.W, Xe, c.N, c.K)[0]
+    assert np.array_equal(col, c.d[:, 1].astype(np.float64) * c.q[:, 40])
+    cols = [12, 3]
+    full = o.gemm_q8_0_f16(c.W, c.X, c.N, c.K)
+    assert np.array_equal(o.gemm_q8_0_f16(c.W, c.X, c.N, c.K, cols=cols), full[:, cols])
+
+
+def pin_sgemm_identity(o):
+    rng = np.random.default_rng(12)
+    A = rng.uniform(-1, 1, (7, 5)).astype(np.float32)
+    I5 = np.eye(5, dtype=np.float32)
+    assert np.array_equal(o.sgemm(A, I5), A.astype(np.float64))
+    B = rng.uniform(-1, 1, (5, 3)).astype(np.float32)
+    E = np.zeros((7, 5), np.float32)
+    E[2, 4] = 1
+    C = o.sgemm(E, B)
+    assert np.array_equal(C[2], B[4].astype(np.float64)) and not C[[0, 1, 3, 4, 5, 6]].any()
+
+
+# ------------------------------------------------------ library-routine pins
+def pin_numpy_crosscheck(o):
+    """Medium shapes against numpy float64 products of weights rebuilt from the
+    generator's integer fields (not from the bytes)."""
+    c = synth.q4_0_case(64, 1024, batch=3, seed=13)
+    W = c.d.astype(np.float64).repeat(32, axis=1) * (c.q.astype(np.float64) - 8)
+    ref = c.x.astype(np.float64) @ W.T
+    y = o.gemv_q4_0(c.W, c.x, c.N, c.K)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+    ck = synth.q4_k_case(32, 1024, batch=2, seed=14)
+    N, nsb = ck.N, ck.K // 256
+    dd = np.repeat(ck.d.astype(np.float64), 256, axis=1)
+    dm = np.repeat(ck.dmin.astype(np.float64), 256, axis=1)
+    sc = np.repeat(ck.sc.reshape(N, nsb * 8).astype(np.float64), 32, axis=1)
+    mm = np.repeat(ck.m.reshape(N, nsb * 8).astype(np.float64), 32, axis=1)
+    Wk = dd * sc * ck.q - dm * mm
+    refk = ck.x.astype(np.float64) @ Wk.T
+    yk = o.gemv_q4_k(ck.W, ck.x, ck.N, ck.K)
+    assert np.allclose(yk, refk, rtol=1e-12, atol=1e-12 * np.abs(refk).max())
+
+    c8 = synth.q8_0_case(24, 40, 512, seed=15)
+    W8 = c8.d.astype(np.float64).repeat(32, axis=1) * c8.q.astype(np.float64)
+    ref8 = c8.X.astype(np.float64) @ W8.T
+    Y8 = o.gemm_q8_0_f16(c8.W, c8.X, c8.N, c8.K)
+    assert np.allclose(Y8, ref8, rtol=1e-12, atol=1e-12 * np.abs(ref8).max())
+
+    s = synth.sgemm_case(33, 47, 129, seed=16)
+    refs = s.A.astype(np.float64) @ s.B.astype(np.float64)
+    Cs = o.sgemm(s.A, s.B)
+    assert np.allclose(Cs, refs, rtol=1e-12, atol=1e-12 * np.abs(refs).max())
+
+
+# ------------------------------------------------------------- brute force
+def _F(v) -> Fraction:
+    return Fraction(float(v))
+
+
+def pin_brute_force(o):
+    """Exact rational sums on tiny shapes; the double oracle agrees to 1e-12
+    relative (only its summation rounds)."""
+    c = synth.q4_0_case(4, 64, batch=2, seed=21)
+    y = o.gemv_q4_0(c.W, c.x, c.N, c.K)
+    for b in range(c.batch):
+        for n in range(c.N):
+            ex = sum(_F(c.d[n, k // 32]) * (int(c.q[n, k]) - 8) * _F(c.x[b, k]) for k in range(c.K))
+            assert abs(Fraction(y[b, n]) - ex) <= Fraction(1, 10**12) * max(abs(ex), Fraction(1, 10**6))
+
+    ck = synth.q4_k_case(3, 256, batch=2, seed=22)
+    yk = o.gemv_q4_k(ck.W, ck.x, ck.N, ck.K)
+    for b in range(ck.batch):
+        for n in range(ck.N):
+            ex = Fraction(0)
+            for k in range(ck.K):
+                s = k // 32
+                w = (_F(ck.d[n, 0]) * int(ck.sc[n, 0, s]) * int(ck.q[n, k])
+                     - _F(ck.dmin[n, 0]) * int(ck.m[n, 0, s]))
+                ex += w * _F(ck.x[b, k])
+            assert abs(Fraction(yk[b, n]) - ex) <= Fraction(1, 10**12) * max(abs(ex), Fraction(1, 10**6))
+
+    c8 = synth.q8_0_case(3, 4, 64, seed=23)
+    Y8 = o.gemm_q8_0_f16(c8.W, c8.X, c8.N, c8.K)
+    for m in range(c8.M):
+        for n in range(c8.N):
+            ex = sum(_F(c8.X[m, k]) * _F(c8.d[n, k // 32]) * int(c8.q[n, k]) for k in range(c8.K))
+            assert abs(Fraction(Y8[m, n]) - ex) <= Fraction(1, 10**12) * max(abs(ex), Fraction(1, 10**6))
+
+    s = synth.sgemm_case(3, 5, 7, seed=24)
+    Cs = o.sgemm(s.A, s.B)
+    for i in range(3):
+        for j in range(5):
+            ex = sum(_F(s.A[i, k]) * _F(s.B[k, j]) for k in range(7))
+            assert abs(Fraction(Cs[i, j]) - ex) <= Fraction(1, 10**12) * max(abs(ex), Fraction(1, 10**6))
+
+
+def pin_subnormal_scales(o):
+    """fp16 subnormal scales are honoured: d = 0x0001 is 2^-24."""
+    j = np.arange(16)
+    q = np.concatenate([j, 15 - j]).astype(np.uint8)[None]
+    d = np.array([[0x0001]], np.uint16).view(np.float16)
+    W = synth.pack_q4_0(d, q)
+    y = o.gemv_q4_0(W, np.ones((1, 32), np.float32), 1, 32)
+    assert y[0, 0] == -16 * 2.0 ** -24
+
+
+PINS = [pin_f16_exhaustive, pin_q4_0_worked, pin_q8_0_worked, pin_q4_k_worked,
+        pin_packers_match_golden, pin_round_trip, pin_closed_forms_q4_0,
+        pin_closed_forms_q4_k, pin_closed_forms_gemm, pin_sgemm_identity,
+        pin_numpy_crosscheck, pin_brute_force, pin_subnormal_scales]
