@@ -1,0 +1,184 @@
+// C entry points of liblqmm: argument validation, launch planning, dispatch.
+// Every check runs on the host before the first HIP call; the only HIP calls
+// are the per-device property query (cached) and the kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdlib.h>
+#include <string.h>
+
+#include "lqmm.h"
+#include "lqmm_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  std::once_flag once;
+  bool ok = false;
+  int num_cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+
+// Current device, checked to be gfx950; CU count cached per device.
+lqmm_status current_device(int *num_cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LQMM_ERR_DEVICE;
+  DeviceInfo &di = g_dev[dev];
+  std::call_once(di.once, [&]() {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return;
+    di.num_cus = prop.multiProcessorCount;
+    di.ok = di.num_cus > 0;
+  });
+  if (!di.ok) return LQMM_ERR_DEVICE;
+  *num_cus = di.num_cus;
+  return LQMM_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool dim_ok(int64_t v) { return v > 0 && v <= LQMM_MAX_DIM; }
+
+// Optional tuning override (benchmark sweeps only): integer env var or -1.
+int env_int(const char *name) {
+  const char *s = getenv(name);
+  if (!s || !*s) return -1;
+  return atoi(s);
+}
+
+lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, float *y,
+                        int64_t N, int64_t K, int64_t batch, hipStream_t stream) {
+  using lqmm::GemvFormat;
+  const int blk = fmt == GemvFormat::Q4_0 ? 32 : 256;
+  const int blk_bytes = fmt == GemvFormat::Q4_0 ? 18 : 144;
+  if (!W || !x || !y) return LQMM_ERR_NULL;
+  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(batch) || K % blk != 0) return LQMM_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(x) || !aligned16(y)) return LQMM_ERR_ALIGN;
+
+  int num_cus = 0;
+  lqmm_status st = current_device(&num_cus);
+  if (st != LQMM_OK) return st;
+
+  const int uw = lqmm::gemv_unit_weights(fmt);
+  const int64_t units_total = K / uw;
+  const int64_t row_bytes = K / blk * blk_bytes;
+  const int threads = lqmm::gemv_threads();
+  const int waves_per_wg = threads / 64;
+  const int env_r = env_int("LQMM_TUNE_GEMV_R");
+  const int env_grid = env_int("LQMM_TUNE_GEMV_GRID");
+
+  for (int64_t b0 = 0; b0 < batch; b0 += 8) {
+    const int B = (int)(batch - b0 < 8 ? batch - b0 : 8);
+    // Units per launch limited by the LDS budget; whole Q4_K super-blocks.
+    int64_t max_units = lqmm::kMaxGemvLds / (int64_t)lqmm::gemv_lds_bytes(fmt, B, 1);
+    if (fmt == GemvFormat::Q4_K) max_units &= ~(int64_t)3;
+    for (int64_t u0 = 0; u0 < units_total; u0 += max_units) {
+      const int64_t nu64 = units_total - u0 < max_units ? units_total - u0 : max_units;
+      const int nu = (int)nu64;
+      lqmm::GemvPlan pl;
+      pl.batch = B;
+      int lpr_log2 = 0;
+      while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
+      pl.lpr_log2 = lpr_log2;
+      const int slots = 64 >> lpr_log2;
+      // Rows per lane: enough row groups to give every CU work, fewer
+      // registers for wide batches.
+      int r = 4;
+      if (B > 4 || (fmt == GemvFormat::Q4_K && B > 2)) r = 2;
+      while (r > 1 && (N + (int64_t)slots * r * waves_per_wg - 1) /
+                              ((int64_t)slots * r * waves_per_wg) < 2 * (int64_t)num_cus)
+        r >>= 1;
+      if (env_r == 1 || env_r == 2 || env_r == 4) r = env_r;
+      pl.rows_per_lane = r;
+      pl.nu = nu;
+      pl.unit0 = u0;
+      pl.row_bytes = row_bytes;
+      pl.ldx = K;
+      pl.ldy = N;
+      pl.N = N;
+      pl.lds_bytes = lqmm::gemv_lds_bytes(fmt, B, nu);
+      const int64_t rows_per_wg = (int64_t)slots * r * waves_per_wg;
+      const int64_t groups = (N + rows_per_wg - 1) / rows_per_wg;
+      int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
+      if (wg_per_cu > 4) wg_per_cu = 4;
+      if (wg_per_cu < 1) wg_per_cu = 1;
+      int64_t grid = groups < num_cus * wg_per_cu ? groups : num_cus * wg_per_cu;
+      if (env_grid > 0) grid = env_grid;
+      pl.grid = (int)grid;
+      pl.accumulate = u0 > 0;
+      const uint8_t *Wb = static_cast<const uint8_t *>(W);
+      hipError_t e = lqmm::gemv_launch(fmt, pl, Wb, x + b0 * K + u0 * uw, y + b0 * N, stream);
+      if (e != hipSuccess) return LQMM_ERR_LAUNCH;
+    }
+  }
+  return LQMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lqmm_status lqmm_sgemm(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+                       void *stream) {
+  if (!A || !B || !C) return LQMM_ERR_NULL;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return LQMM_ERR_SHAPE;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return LQMM_ERR_ALIGN;
+  int num_cus = 0;
+  lqmm_status st = current_device(&num_cus);
+  if (st != LQMM_OK) return st;
+  hipError_t e = lqmm::sgemm_launch(A, B, C, M, N, K, num_cus, (hipStream_t)stream);
+  return e == hipSuccess ? LQMM_OK : LQMM_ERR_LAUNCH;
+}
+
+lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                           int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return gemv_common(lqmm::GemvFormat::Q4_0, W, x, y, N, K, batch, (hipStream_t)stream);
+}
+
+lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                           int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return gemv_common(lqmm::GemvFormat::Q4_K, W, x, y, N, K, batch, (hipStream_t)stream);
+}
+
+lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, int64_t M,
+                               int64_t N, int64_t K, void *stream) {
+  if (!W || !X || !Y) return LQMM_ERR_NULL;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || K % 32 != 0) return LQMM_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LQMM_ERR_ALIGN;
+  int num_cus = 0;
+  lqmm_status st = current_device(&num_cus);
+  if (st != LQMM_OK) return st;
+  hipError_t e = lqmm::gemm_q8_0_launch(static_cast<const uint8_t *>(W), X, Y, M, N, K, num_cus,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? LQMM_OK : LQMM_ERR_LAUNCH;
+}
+
+size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
+  (void)N;
+  (void)K;
+  (void)batch;
+  return 0;
+}
+
+const char *lqmm_status_string(lqmm_status s) {
+  switch (s) {
+    case LQMM_OK: return "LQMM_OK";
+    case LQMM_ERR_NULL: return "LQMM_ERR_NULL: a required pointer is NULL";
+    case LQMM_ERR_SHAPE: return "LQMM_ERR_SHAPE: a size is out of range or not a block multiple";
+    case LQMM_ERR_ALIGN: return "LQMM_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case LQMM_ERR_WORKSPACE: return "LQMM_ERR_WORKSPACE: workspace argument inconsistent";
+    case LQMM_ERR_DEVICE: return "LQMM_ERR_DEVICE: no usable gfx950 device";
+    case LQMM_ERR_LAUNCH: return "LQMM_ERR_LAUNCH: kernel launch failed";
+  }
+  return "LQMM: unknown status";
+}
+
+int lqmm_version(void) { return 100; }
+
+}  // extern "C"

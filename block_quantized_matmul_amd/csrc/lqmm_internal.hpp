@@ -1,0 +1,45 @@
+// Host-side interface between the C entry points (api.hip) and the kernel
+// translation units. Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lqmm {
+
+// ---- GEMV -------------------------------------------------------------------
+enum class GemvFormat { Q4_0, Q4_K };
+
+// Largest dynamic LDS one GEMV launch may use (staged activations + sums).
+constexpr int kMaxGemvLds = 144 * 1024;
+
+struct GemvPlan {
+  int batch;          // activation rows in this launch, 1..8
+  int rows_per_lane;  // 1, 2 or 4
+  int lpr_log2;       // log2(lanes sharing one weight row)
+  int nu;             // units (of gemv_unit_weights weights) per row in this launch
+  int64_t unit0;      // first unit of each row covered by this launch
+  int64_t row_bytes;  // bytes per weight row
+  int64_t ldx, ldy;   // row strides of x and y, in elements
+  int64_t N;          // weight rows
+  int grid;           // workgroups
+  size_t lds_bytes;   // dynamic LDS
+  int accumulate;     // 1: y += result
+};
+
+size_t gemv_lds_bytes(GemvFormat f, int batch, int nu);
+int gemv_unit_weights(GemvFormat f);
+int gemv_threads();
+hipError_t gemv_launch(GemvFormat f, const GemvPlan &plan, const uint8_t *W, const float *x,
+                       float *y, hipStream_t stream);
+
+// ---- Q8_0 x fp16 GEMM ---------------------------------------------------------
+hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,
+                            int64_t N, int64_t K, int num_cus, hipStream_t stream);
+
+// ---- fp32 GEMM ----------------------------------------------------------------
+hipError_t sgemm_launch(const float *A, const float *B, float *C, int64_t M, int64_t N,
+                        int64_t K, int num_cus, hipStream_t stream);
+
+}  // namespace lqmm

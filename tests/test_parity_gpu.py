@@ -1,0 +1,256 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+the same seeded inputs, element by element.
+
+Bars: relative Frobenius and normalized max-abs error <= 1e-5 / 1e-4 for the
+fp32 GEMM and <= 2e-3 for the quantized GEMVs and the Q8_0 x fp16 GEMM;
+bit-exact where the arithmetic is exact (one-hot activations, identity
+matrices). Full benchmark sizes are checked in the launch configuration the
+benchmark uses (the library picks it from the shape), on all outputs where
+the oracle is cheap and on sampled outputs otherwise.
+"""
+import numpy as np
+import pytest
+
+import block_quantized_matmul_amd as bq
+import synth
+from gpu_util import TOL_FP32, TOL_QUANT, announce, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bq.load()
+
+
+def _run_q4_0(c):
+    y = bq.lqmm_gemv_q4_0(dev(c.W.reshape(-1)), dev(c.x), c.N)
+    return host(y)
+
+
+def _run_q4_k(c):
+    y = bq.lqmm_gemv_q4_k(dev(c.W.reshape(-1)), dev(c.x), c.N)
+    return host(y)
+
+
+# ----------------------------------------------------------------- Q4_0 GEMV
+Q4_0_SMALL = [(1, 32, 1), (7, 32, 3), (5, 64, 2), (13, 96, 1), (33, 288, 5), (64, 1024, 8),
+              (100, 4096, 4), (1, 4096, 9), (3, 9216, 8), (257, 2048, 16), (2, 160, 7),
+              (1000, 512, 1), (31, 8192, 2)]
+
+
+@pytest.mark.parametrize("N,K,B", Q4_0_SMALL)
+def test_q4_0_small(orc, N, K, B):
+    c = synth.q4_0_case(N, K, B, seed=N * 7 + K + B)
+    announce(f"q4_0 gemv N={N} K={K} batch={B}")
+    y = _run_q4_0(c)
+    ref = orc.gemv_q4_0(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"q4_0 {N}x{K} b{B}")
+
+
+@pytest.mark.parametrize("name", ["q4_0_gemv_1024", "q4_0_gemv_4096x4096_b1",
+                                  "q4_0_gemv_4096x4096_b4", "q4_0_gemv_11008x4096_b1",
+                                  "q4_0_gemv_11008x4096_b4", "q4_0_gemv_12288x4096_b1",
+                                  "q4_0_gemv_12288x4096_b4"])
+def test_q4_0_configs(orc, name):
+    c = synth.make(name)
+    announce(f"{name}")
+    y = _run_q4_0(c)
+    ref = orc.gemv_q4_0(c.W, c.x, c.N, c.K)
+    assert_close(y, ref, TOL_QUANT, name)
+
+
+def test_q4_0_one_hot_exact(orc):
+    """One-hot activations extract weight columns exactly (x = 1 is exact in
+    fp16 and every partial sum is an exact small integer)."""
+    c = synth.make("q4_0_gemv_1024")
+    ks = [0, 1, 15, 16, 17, 31, 32, 500, 1007, 1023]
+    x = np.zeros((len(ks), c.K), np.float32)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    announce("q4_0 one-hot exactness")
+    y = host(bq.lqmm_gemv_q4_0(dev(c.W.reshape(-1)), dev(x), c.N))
+    ref = orc.gemv_q4_0(c.W, x, c.N, c.K)
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+def test_q4_0_subnormal_scales(orc):
+    """Subnormal fp16 scales are honoured (not flushed)."""
+    N, K = 64, 256
+    rng = np.random.default_rng(5)
+    d = rng.integers(1, 1024, size=(N, K // 32)).astype(np.uint16).view(np.float16)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    W = synth.pack_q4_0(d, q)
+    x = np.eye(K, dtype=np.float32)[[0, 20, 77, 255]]
+    announce("q4_0 subnormal scales")
+    y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x), N))
+    ref = orc.gemv_q4_0(W, x, N, K)
+    assert np.array_equal(y, ref.astype(np.float32))
+    xr = rng.standard_normal((2, K)).astype(np.float32)
+    y2 = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(xr), N))
+    assert_close(y2, orc.gemv_q4_0(W, xr, N, K), TOL_QUANT, "subnormal random x")
+
+
+def test_q4_0_batch_rows_match_single(orc):
+    c = synth.q4_0_case(300, 4096, 4, seed=9)
+    announce("q4_0 batch consistency")
+    yb = _run_q4_0(c)
+    for b in range(4):
+        y1 = host(bq.lqmm_gemv_q4_0(dev(c.W.reshape(-1)), dev(c.x[b]), c.N))
+        assert_close(y1, yb[b], (1e-6, 1e-6), f"row {b}")
+
+
+def test_q4_0_deterministic():
+    c = synth.make("q4_0_gemv_4096x4096_b4")
+    W, x = dev(c.W.reshape(-1)), dev(c.x)
+    announce("q4_0 determinism")
+    ys = [host(bq.lqmm_gemv_q4_0(W, x, c.N)) for _ in range(5)]
+    for y in ys[1:]:
+        assert np.array_equal(y, ys[0])
+
+
+# ----------------------------------------------------------------- Q4_K GEMV
+Q4_K_SMALL = [(1, 256, 1), (3, 512, 2), (17, 768, 8), (5, 256, 9), (9, 8704, 8),
+              (70, 2048, 3), (129, 4096, 5), (2, 1280, 4), (40, 16384, 1), (257, 256, 6)]
+
+
+@pytest.mark.parametrize("N,K,B", Q4_K_SMALL)
+def test_q4_k_small(orc, N, K, B):
+    c = synth.q4_k_case(N, K, B, seed=N * 3 + K + B)
+    announce(f"q4_k gemv N={N} K={K} batch={B}")
+    y = _run_q4_k(c)
+    ref = orc.gemv_q4_k(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"q4_k {N}x{K} b{B}")
+
+
+@pytest.mark.parametrize("name", ["q4_k_gemv_28672x8192_b1", "q4_k_gemv_28672x8192_b8"])
+def test_q4_k_configs(orc, name):
+    c = synth.make(name)
+    announce(name)
+    y = _run_q4_k(c)
+    ref = orc.gemv_q4_k(c.W, c.x, c.N, c.K)
+    assert_close(y, ref, TOL_QUANT, name)
+
+
+def test_q4_k_one_hot_exact(orc):
+    c = synth.q4_k_case(300, 2048, 1, seed=31)
+    ks = [0, 31, 32, 63, 64, 200, 255, 256, 1500, 2047]
+    x = np.zeros((len(ks), c.K), np.float32)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    announce("q4_k one-hot exactness")
+    y = host(bq.lqmm_gemv_q4_k(dev(c.W.reshape(-1)), dev(x[:8]), c.N))
+    ref = orc.gemv_q4_k(c.W, x[:8], c.N, c.K)
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+def test_q4_k_extreme_codes(orc):
+    """sc, m at 0 and 63, q at 0 and 15, subnormal d and dmin."""
+    N, K = 48, 512
+    rng = np.random.default_rng(8)
+    nsb = K // 256
+    d = rng.integers(1, 0x3C00, size=(N, nsb)).astype(np.uint16).view(np.float16)
+    dmin = rng.integers(1, 0x0400, size=(N, nsb)).astype(np.uint16).view(np.float16)
+    sc = rng.choice([0, 1, 62, 63], size=(N, nsb, 8)).astype(np.uint8)
+    m = rng.choice([0, 1, 62, 63], size=(N, nsb, 8)).astype(np.uint8)
+    q = rng.choice([0, 15], size=(N, K)).astype(np.uint8)
+    W = synth.pack_q4_k(d, dmin, sc, m, q)
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    announce("q4_k extreme codes")
+    y = host(bq.lqmm_gemv_q4_k(dev(W.reshape(-1)), dev(x), N))
+    assert_close(y, orc.gemv_q4_k(W, x, N, K), TOL_QUANT, "q4_k extremes")
+
+
+# ------------------------------------------------------------- Q8_0 GEMM
+Q8_0_SMALL = [(1, 1, 32), (3, 5, 64), (17, 130, 96), (128, 128, 64), (130, 257, 320),
+              (64, 200, 4096), (256, 512, 1024), (1, 300, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", Q8_0_SMALL)
+def test_q8_0_small(orc, M, N, K):
+    c = synth.q8_0_case(M, N, K, seed=M + N + K)
+    announce(f"q8_0 gemm M={M} N={N} K={K}")
+    Y = host(bq.lqmm_gemm_q8_0_f16(dev(c.W.reshape(-1)), dev(c.X), N)).astype(np.float64)
+    ref = orc.gemm_q8_0_f16(c.W, c.X, N, K)
+    assert_close(Y, ref, TOL_QUANT, f"q8_0 {M}x{N}x{K}")
+
+
+def test_q8_0_config_sampled(orc):
+    c = synth.make("q8_0_gemm_512x14336x4096")
+    announce("q8_0 gemm 512x14336x4096")
+    Y = host(bq.lqmm_gemm_q8_0_f16(dev(c.W.reshape(-1)), dev(c.X), c.N)).astype(np.float64)
+    rng = np.random.default_rng(0)
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 223, 224, 7167, 7168, c.N - 1],
+                                     rng.choice(c.N, 247, replace=False)]))
+    ref = orc.gemm_q8_0_f16(c.W, c.X, c.N, c.K, cols=cols)
+    assert_close(Y[:, cols], ref, TOL_QUANT, "q8_0 config (sampled columns)")
+    assert np.isfinite(Y).all()
+
+
+def test_q8_0_one_hot_exact(orc):
+    """A one-hot X row returns fp16(d*q) exactly: one rounding of the weight,
+    exact products and sums."""
+    c = synth.q8_0_case(8, 96, 256, seed=3)
+    X = np.zeros((8, c.K), np.float16)
+    for i, k in enumerate([0, 5, 31, 32, 100, 200, 254, 255]):
+        X[i, k] = 1.0
+    announce("q8_0 one-hot exactness")
+    Y = host(bq.lqmm_gemm_q8_0_f16(dev(c.W.reshape(-1)), dev(X), c.N))
+    ref = orc.gemm_q8_0_f16(c.W, X, c.N, c.K)
+    assert np.array_equal(Y, ref.astype(np.float16))
+
+
+# --------------------------------------------------------------- fp32 GEMM
+SGEMM_SMALL = [(1, 1, 1), (3, 5, 7), (17, 33, 65), (127, 129, 130), (128, 128, 128),
+               (200, 64, 3), (64, 256, 1000), (5, 300, 33)]
+
+
+@pytest.mark.parametrize("M,N,K", SGEMM_SMALL)
+def test_sgemm_small(orc, M, N, K):
+    s = synth.sgemm_case(M, N, K, seed=M * N + K)
+    announce(f"sgemm M={M} N={N} K={K}")
+    C = host(bq.lqmm_sgemm(dev(s.A), dev(s.B)))
+    ref = orc.sgemm(s.A, s.B)
+    assert_close(C, ref, TOL_FP32, f"sgemm {M}x{N}x{K}")
+
+
+def test_sgemm_config_sampled(orc):
+    s = synth.make("sgemm_2048")
+    announce("sgemm 2048^3")
+    C = host(bq.lqmm_sgemm(dev(s.A), dev(s.B)))
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 1023, 1024, 2047],
+                                     rng.choice(s.M, 55, replace=False)]))
+    ref = orc.sgemm(s.A, s.B, rows=rows)
+    assert_close(C[rows], ref, TOL_FP32, "sgemm config (sampled rows)")
+    assert np.isfinite(C).all()
+
+
+def test_sgemm_identity_exact():
+    rng = np.random.default_rng(2)
+    A = rng.uniform(-1, 1, (150, 130)).astype(np.float32)
+    I = np.eye(130, dtype=np.float32)
+    announce("sgemm identity exactness")
+    C = host(bq.lqmm_sgemm(dev(A), dev(I)))
+    assert np.array_equal(C, A)
+
+
+def test_errors_raise_on_device():
+    import torch
+    W = torch.zeros(18 * 4, dtype=torch.uint8, device="cuda:0")
+    x = torch.zeros((1, 48), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError):
+        bq.lqmm_gemv_q4_0(W, x, 4)
+    # a contiguous view whose data pointer is only 4-byte aligned: the
+    # library itself rejects it
+    xs = torch.zeros((1, 33), dtype=torch.float32, device="cuda:0")[:, 1:]
+    with pytest.raises(bq.LqmmError) as e:
+        bq.lqmm_gemv_q4_0(W[:18 * 4], xs, 4)
+    assert e.value.status == 3
+    # a strided (non-contiguous) activation is refused by the binding
+    xn = torch.zeros((2, 64), dtype=torch.float32, device="cuda:0")[:, ::2]
+    with pytest.raises(ValueError):
+        bq.lqmm_gemv_q4_0(W, xn, 4)
