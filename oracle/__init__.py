@@ -57,7 +57,13 @@ class Oracle:
         lib.lqmm_oracle_gemm_q8_0_f16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
         lib.lqmm_oracle_sgemm.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
         lib.lqmm_oracle_mutant.restype = ctypes.c_int
+        lib.lqmm_oracle_threads.restype = ctypes.c_int
         self.lib = lib
+
+    @property
+    def threads(self) -> int:
+        """OpenMP threads the oracle's loops use."""
+        return self.lib.lqmm_oracle_threads()
 
     @property
     def mutant(self) -> int:

@@ -48,6 +48,7 @@
  * that the pins catch such mistakes.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -304,6 +305,9 @@ void lqmm_oracle_sgemm(const float *A, const float *B, double *C, int64_t M, int
   }
   free(Bt);
 }
+
+/* Threads the OpenMP loops above use. */
+int lqmm_oracle_threads(void) { return omp_get_max_threads(); }
 
 /* Mutant id this library was built with (0 = the real oracle). */
 int lqmm_oracle_mutant(void) { return LQMM_ORACLE_MUTANT; }
