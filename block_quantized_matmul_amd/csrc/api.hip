@@ -67,44 +67,108 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   const int threads = lqmm::gemv_threads();
   const int waves_per_wg = threads / 64;
   const int env_r = env_int("LQMM_TUNE_GEMV_R");
+  const int env_u = env_int("LQMM_TUNE_GEMV_U");
   const int env_grid = env_int("LQMM_TUNE_GEMV_GRID");
+  const int env_mfma = env_int("LQMM_TUNE_GEMV_MFMA");
+  const int env_wgcu = env_int("LQMM_TUNE_GEMV_WG_PER_CU");
+  const int env_ks = env_int("LQMM_TUNE_GEMV_KS");
+  const int env_waves = env_int("LQMM_TUNE_GEMV_WAVES");
+  const int env_ldsk = env_int("LQMM_TUNE_GEMV_LDSK");
+  const int env_depth = env_int("LQMM_TUNE_GEMV_DEPTH");
 
-  for (int64_t b0 = 0; b0 < batch; b0 += 8) {
-    const int B = (int)(batch - b0 < 8 ? batch - b0 : 8);
+  for (int64_t b0 = 0; b0 < batch; ) {
+    const int64_t left = batch - b0;
+    // Matrix cores from three activation rows up: their cost per weight does
+    // not grow with the batch, the dot2 path's does.
+    bool mfma = left >= 3;
+    if (env_mfma == 0 || env_mfma == 1) mfma = env_mfma == 1;
+    const int bmax = mfma ? 16 : 2;
+    const int B = (int)(left < bmax ? left : bmax);
     // Units per launch limited by the LDS budget; whole Q4_K super-blocks.
-    int64_t max_units = lqmm::kMaxGemvLds / (int64_t)lqmm::gemv_lds_bytes(fmt, B, 1);
+    // Q4_K in MFMA mode: coalesced loads staged through LDS (8 waves, one
+    // super-block per row per chunk) unless disabled for tuning.
+    const bool lds_stage = mfma && fmt == GemvFormat::Q4_K && env_ldsk != 0;
+    // Other MFMA launches: 16-wave workgroups when the staged activations
+    // leave room for only one workgroup per CU, so that more loads are in
+    // flight.
+    int waves = 8;
+    if (mfma && !lds_stage) {
+      const int64_t per_unit = (int64_t)lqmm::gemv_lds_bytes(fmt, true, B, 1);
+      if (per_unit * units_total > 80 * 1024) waves = 16;
+      if (env_waves == 8 || env_waves == 16) waves = env_waves;
+    }
+    const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2) ? env_u : 1) : 0;
+    const int64_t red_bytes =
+        mfma ? (int64_t)lqmm::gemv_mfma_reduce_bytes(waves) +
+                   (lds_stage ? (int64_t)lqmm::gemv_q4k_lds_stage_bytes(lds_u) : 0)
+             : 0;
+    const int64_t lds_cap = lds_stage ? lqmm::kMaxLds : lqmm::kMaxGemvLds;
+    int64_t max_units = (lds_cap - red_bytes) / (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, 1);
     if (fmt == GemvFormat::Q4_K) max_units &= ~(int64_t)3;
     for (int64_t u0 = 0; u0 < units_total; u0 += max_units) {
       const int64_t nu64 = units_total - u0 < max_units ? units_total - u0 : max_units;
       const int nu = (int)nu64;
       lqmm::GemvPlan pl;
+      pl.mfma = mfma;
       pl.batch = B;
       int lpr_log2 = 0;
       while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
       pl.lpr_log2 = lpr_log2;
-      const int slots = 64 >> lpr_log2;
-      // Rows per lane: enough row groups to give every CU work, fewer
-      // registers for wide batches.
-      int r = 4;
-      if (B > 4 || (fmt == GemvFormat::Q4_K && B > 2)) r = 2;
-      while (r > 1 && (N + (int64_t)slots * r * waves_per_wg - 1) /
-                              ((int64_t)slots * r * waves_per_wg) < 2 * (int64_t)num_cus)
-        r >>= 1;
-      if (env_r == 1 || env_r == 2 || env_r == 4) r = env_r;
-      pl.rows_per_lane = r;
+      pl.lds_bytes = lqmm::gemv_lds_bytes(fmt, mfma, B, nu) + red_bytes;
+      int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
+      const int64_t wg_cap = env_wgcu > 0 ? env_wgcu : 2;
+      if (wg_per_cu > wg_cap) wg_per_cu = wg_cap;
+      if (wg_per_cu < 1) wg_per_cu = 1;
+      int64_t wg_needed;
+      if (mfma) {
+        // R = 1 tile of 16 rows per team; KS waves share a tile along K so
+        // that small N still gives every CU several waves.
+        const int64_t tiles = (N + 15) / 16;
+        int uu = lds_stage ? lds_u : 2, ks = waves == 16 ? 4 : 1;
+        const int ksmax = waves == 16 ? 16 : 8;
+        while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
+        if (!lds_stage && (env_u == 2 || env_u == 4)) uu = env_u;
+        if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
+          ks = env_ks;
+        // every slice must hold whole chunks of 4*uu units
+        if (lds_stage) {
+          while (ks > 1 && (nu / ks) < 4 * uu) ks /= 2;
+          if (nu < 4 * uu) uu = 1;
+        }
+        pl.rows_per_lane = 1;
+        pl.units_per_lane = uu;
+        pl.ksplit = ks;
+        pl.waves = waves;
+        pl.lds_stage = lds_stage;
+        pl.depth = env_depth > 0 ? env_depth : (uu == 1 ? 4 : 2);
+        const int teams = waves / ks;
+        wg_needed = (tiles + teams - 1) / teams;
+      } else {
+        const int slots = 64 >> lpr_log2;
+        // Rows per lane R and units per lane per chunk U.
+        int r = 2, uu = 1;
+        if (env_r == 1 || env_r == 2) r = env_r;
+        if (env_u == 1 || env_u == 2 || env_u == 4) uu = env_u;
+        if (r == 1 && uu == 1) uu = 2;
+        if (r == 2 && uu == 4) uu = 2;
+        pl.rows_per_lane = r;
+        pl.units_per_lane = uu;
+        pl.ksplit = 1;
+        pl.waves = waves_per_wg;
+        pl.lds_stage = 0;
+        pl.depth = 2;
+        const int64_t groups = (N + (int64_t)slots * r - 1) / ((int64_t)slots * r);
+        wg_needed = (groups + waves_per_wg - 1) / waves_per_wg;
+      }
       pl.nu = nu;
       pl.unit0 = u0;
       pl.row_bytes = row_bytes;
       pl.ldx = K;
       pl.ldy = N;
       pl.N = N;
-      pl.lds_bytes = lqmm::gemv_lds_bytes(fmt, B, nu);
-      const int64_t rows_per_wg = (int64_t)slots * r * waves_per_wg;
-      const int64_t groups = (N + rows_per_wg - 1) / rows_per_wg;
-      int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
-      if (wg_per_cu > 4) wg_per_cu = 4;
-      if (wg_per_cu < 1) wg_per_cu = 1;
-      int64_t grid = groups < num_cus * wg_per_cu ? groups : num_cus * wg_per_cu;
+      // Persistent grid: at most wg_per_cu workgroups per CU, no more than
+      // there is work for.
+      int64_t grid = wg_needed < num_cus * wg_per_cu ? wg_needed : num_cus * wg_per_cu;
       if (env_grid > 0) grid = env_grid;
       pl.grid = (int)grid;
       pl.accumulate = u0 > 0;
@@ -112,6 +176,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       hipError_t e = lqmm::gemv_launch(fmt, pl, Wb, x + b0 * K + u0 * uw, y + b0 * N, stream);
       if (e != hipSuccess) return LQMM_ERR_LAUNCH;
     }
+    b0 += B;
   }
   return LQMM_OK;
 }

@@ -7,26 +7,33 @@
 // multiplies them with the activations. The quantization format is a
 // compile-time trait (the page's "dequantization chosen at compile time").
 //
-// Design for CDNA4:
-// * A workgroup (512 threads) first stages its activations in LDS as fp16,
-//   in the exact pair order the nibble unpacker produces (below), together
-//   with per-unit sums of the staged values. It then walks rows with a grid
-//   stride; every wave reads weights straight from HBM into registers.
-// * A "unit" is the run of weights one lane handles per row: one Q4_0 block
-//   (32 weights, 18 bytes) or a quarter of a Q4_K super-block (64 weights:
-//   the 16-byte header plus 32 bytes of nibbles). Consecutive lanes take
-//   consecutive units, so each wave-wide load covers one contiguous span.
-//   LPR lanes share a row (LPR = units per row rounded up to a power of two,
-//   at most 64) and their partial sums are combined with DPP.
-// * Nibble unpacking uses the fp16 exponent trick: OR-ing a nibble into the
-//   mantissa of 1024.0 (0x6400) gives the exact fp16 value 1024 + q (low
-//   nibble) or 1024 + 16q (high nibble) with one v_and_or_b32 per pair. The
-//   bias terms are removed with the staged sums, and high-nibble pairs are
-//   matched with activations pre-scaled by 1/16. Two fp16 products are
-//   accumulated in fp32 by v_dot2_f32_f16; the block scales are applied in
-//   fp32 once per unit.
-// * Each lane handles R rows per unit so an activation word read from LDS is
-//   used R times.
+// Common structure (both modes):
+// * A "unit" is the run of weights one lane takes from one weight row: one
+//   Q4_0 block (32 weights, 18 bytes) or a quarter of a Q4_K super-block (64
+//   weights: the 16-byte header plus 32 bytes of nibbles).
+// * A workgroup (512 threads) stages the activations in LDS as fp16, then its
+//   waves stream weight rows with a grid stride. Each wave walks "groups" of
+//   rows in "chunks" of U units per lane through two register buffers: the
+//   next chunk loads while the current one is computed. The first chunk is
+//   requested before the activations are staged.
+// * Nibbles become fp16 with the exponent trick: OR-ing a nibble into the
+//   mantissa of 1024.0 (0x6400) gives the exact value 1024 + q (low nibble)
+//   or 1024 + 16q (high nibble), one v_and_or_b32 per pair of weights.
+//
+// VALU mode (batch 1..8, used for 1..2): consecutive lanes take consecutive
+// units of the same row(s) (LPR lanes per row), the activation pairs are
+// multiplied with v_dot2_f32_f16 into fp32, the 1024 biases are removed with
+// staged activation sums, block scales are applied in fp32 once per unit and
+// the LPR lane partials are summed with DPP.
+//
+// MFMA mode (batch up to 16 per launch, used from 3 up): a wave covers 16
+// weight rows at once. Lane l takes row l % 16 and unit offset l / 16, which
+// is exactly the B-operand layout of v_mfma_f32_16x16x32_f16 (column = weight
+// row, 8 k values per lane); the nibbles of each 32-bit word are dequantized
+// to fp16 weights in registers (one rounding per weight) and fed to the MFMA
+// with the staged activations (row = batch row) as the A operand. The matrix
+// core does the k reduction, so the per-weight VALU cost no longer grows with
+// the batch.
 #include "lqmm_device.hpp"
 #include "lqmm_internal.hpp"
 
@@ -34,31 +41,58 @@ namespace lqmm {
 namespace {
 
 constexpr int kGemvThreads = 512;
+constexpr int kWavesPerWg = kGemvThreads / kWave;
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
 
 // Unpack one 32-bit word of nibbles (bytes e = 0..3, each holding a "lo"
 // nibble and a "hi" nibble) into four fp16 pairs:
-//   P0 = (1024+lo0, 1024+lo2)      P1 = (1024+16hi0, 1024+16hi2)
-//   P2 = (1024+lo1, 1024+lo3)      P3 = (1024+16hi1, 1024+16hi3)
+//   p0 = (1024+lo0, 1024+lo2)      p1 = (1024+16hi0, 1024+16hi2)
+//   p2 = (1024+lo1, 1024+lo3)      p3 = (1024+16hi1, 1024+16hi3)
+// The staged activation word uses the same order: (x_lo0, x_lo2),
+// (x_hi0, x_hi2), (x_lo1, x_lo3), (x_hi1, x_hi3).
 struct Nibbles {
   half2_t p0, p1, p2, p3;
 };
-__device__ __forceinline__ Nibbles unpack_word(uint32_t v) {
+
+// (a & m) | o as one v_and_or_b32. Written out because the VOP3 encoding
+// cannot take the two 32-bit literal masks, and with them inline the compiler
+// splits every pair into a v_and_b32 and a v_or_b32; here the masks live in
+// VGPRs (see UnpackMasks).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// The unpack constants, materialized once per kernel in VGPRs.
+struct UnpackMasks {
+  uint32_t lo, hi, magic;
+  __device__ __forceinline__ UnpackMasks() : lo(0x000F000Fu), hi(0x00F000F0u), magic(kMagic) {
+    asm volatile("" : "+v"(lo), "+v"(hi), "+v"(magic));
+  }
+};
+
+__device__ __forceinline__ Nibbles unpack_word(uint32_t v, const UnpackMasks &k) {
   uint32_t v8 = v >> 8;
   Nibbles n;
-  n.p0 = as_half2((v & 0x000F000Fu) | kMagic);
-  n.p1 = as_half2((v & 0x00F000F0u) | kMagic);
-  n.p2 = as_half2((v8 & 0x000F000Fu) | kMagic);
-  n.p3 = as_half2((v8 & 0x00F000F0u) | kMagic);
+  n.p0 = as_half2(and_or(v, k.lo, k.magic));
+  n.p1 = as_half2(and_or(v, k.hi, k.magic));
+  n.p2 = as_half2(and_or(v8, k.lo, k.magic));
+  n.p3 = as_half2(and_or(v8, k.hi, k.magic));
   return n;
+}
+
+__device__ __forceinline__ half2_t h2(float v) { return half2_t{(half_t)v, (half_t)v}; }
+__device__ __forceinline__ half2_t pk_fma(half2_t a, half2_t b, half2_t c) {
+  return __builtin_elementwise_fma(a, b, c);
+}
+__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // ---- Q4_0: unit = one block of 32 weights ----------------------------------
 // Word t (t = 0..3) of the block's qs holds lo positions 4t..4t+3 and hi
-// positions 16+4t..16+4t+3. The staged sums hold, per unit and batch row,
-// -(1032*S_lo + 1152*S_hi) where S_lo is the sum of the staged lo values and
-// S_hi the sum of the staged (x/16) hi values; then
-//   sum_j (q_j - 8) x_j = staged + sum of the dot products.
+// positions 16+4t..16+4t+3.
 struct FmtQ4_0 {
   static constexpr int kUnitWeights = 32;
   static constexpr int kWords = 4;
@@ -67,8 +101,13 @@ struct FmtQ4_0 {
     u32x4 q;
     uint32_t d;
   };
-  static __device__ __forceinline__ Raw load(const uint8_t *row, int64_t unit) {
-    const uint8_t *p = row + unit * 18;
+  struct Prep {
+    half2_t d2;
+  };
+  // Byte offset of unit `unit` (a multiple of 4 for Q4_K) in a row.
+  static __host__ __device__ __forceinline__ int64_t unit_offset(int64_t unit) { return unit * 18; }
+  static __device__ __forceinline__ Raw load(const uint8_t *row, uint32_t unit) {
+    const uint8_t *p = row + unit * 18u;
     Raw r;
     r.q = load_u32x4_unaligned(p + 2);
     r.d = load_u16(p);
@@ -80,14 +119,19 @@ struct FmtQ4_0 {
     r.d = 0;
     return r;
   }
+  static __device__ __forceinline__ uint32_t word(const Raw &r, int t) { return r.q[t]; }
+
+  // VALU mode. Staged sum per (unit, batch row): -(1032*S_lo + 1152*S_hi) with
+  // S_lo the sum of the staged lo values and S_hi of the staged x/16 hi
+  // values, so that sum_j (q_j - 8) x_j = staged + the dot products.
   static __device__ __forceinline__ void stage_sums(float *sums, int idx, float slo, float shi) {
     sums[idx] = -(1032.0f * slo + 1152.0f * shi);
   }
-
+  // u must index a staged unit; `valid` = 0 makes the unit contribute 0.
   template <int B, int R>
   static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs,
-                                                 const float *sums, int u, int nu,
-                                                 float (&acc)[R][B]) {
+                                                 const float *sums, int u, int nu, bool valid,
+                                                 const UnpackMasks &k, float (&acc)[R][B]) {
     float s[R][B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -102,7 +146,7 @@ struct FmtQ4_0 {
       for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * nu + u];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        Nibbles n = unpack_word(raw[r].q[t]);
+        Nibbles n = unpack_word(raw[r].q[t], k);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           float a = s[r][b];
@@ -116,10 +160,36 @@ struct FmtQ4_0 {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float d = f16_bits_to_f32(raw[r].d);
+      float d = valid ? f16_bits_to_f32(raw[r].d) : 0.0f;
 #pragma unroll
       for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, s[r][b], acc[r][b]);
     }
+  }
+
+  // MFMA mode: fp16 weights d*(q-8) of word t (exact q-8, one rounding);
+  // valid == false yields zero weights.
+  static __device__ __forceinline__ Prep prep(const Raw &r, int /*pair*/, bool valid) {
+    Prep p;
+    p.d2 = as_half2(valid ? (r.d & 0xFFFFu) * 0x10001u : 0u);
+    return p;
+  }
+  static __device__ __forceinline__ u32x4 dequant(const Raw &r, const Prep &p, int t,
+                                                 const UnpackMasks &k) {
+    Nibbles n = unpack_word(r.q[t], k);
+    const half2_t lo_bias = h2(-1032.0f), sixteenth = h2(0.0625f), hi_bias = h2(-72.0f);
+    u32x4 w;
+    w.x = as_u32((n.p0 + lo_bias) * p.d2);
+    w.y = as_u32(pk_fma(n.p1, sixteenth, hi_bias) * p.d2);
+    w.z = as_u32((n.p2 + lo_bias) * p.d2);
+    w.w = as_u32(pk_fma(n.p3, sixteenth, hi_bias) * p.d2);
+    return w;
+  }
+  // U consecutive units starting at `unit`, each clamped to `last`.
+  template <int U>
+  static __device__ __forceinline__ void load_units(const uint8_t *row, uint32_t unit,
+                                                    uint32_t last, Raw (&out)[U]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) out[j] = load(row, unit + j <= last ? unit + j : last);
   }
 };
 
@@ -127,9 +197,7 @@ struct FmtQ4_0 {
 // Lane unit u of a row is sub-block pair i = u % 4 of super-block u / 4.
 // Word t (t = 0..7) of the pair's 32 qs bytes holds sub-block 2i weights
 // 4t..4t+3 (low nibbles, "lo") and sub-block 2i+1 weights 4t..4t+3 (high
-// nibbles, "hi"). The staged sums are (-1024*S_lo, -1024*S_hi) per unit and
-// batch row, which remove the 1024 bias of each dot product; they also give
-// the activation sums needed by the dmin * m term.
+// nibbles, "hi").
 struct FmtQ4_K {
   static constexpr int kUnitWeights = 64;
   static constexpr int kWords = 8;
@@ -139,9 +207,15 @@ struct FmtQ4_K {
     u32x4 q0;  // qs words 0..3 of the pair
     u32x4 q1;  // qs words 4..7
   };
-  static __device__ __forceinline__ Raw load(const uint8_t *row, int64_t unit) {
-    const uint8_t *sb = row + (unit >> 2) * 144;
-    const uint8_t *qs = sb + 16 + (unit & 3) * 32;
+  struct Prep {
+    half2_t dsc_lo, dmm_lo, dsc_hi, dmm_hi;
+  };
+  static __host__ __device__ __forceinline__ int64_t unit_offset(int64_t unit) {
+    return (unit >> 2) * 144;
+  }
+  static __device__ __forceinline__ Raw load(const uint8_t *row, uint32_t unit) {
+    const uint8_t *sb = row + (unit >> 2) * 144u;
+    const uint8_t *qs = sb + 16 + (unit & 3u) * 32u;
     Raw r;
     r.h = *reinterpret_cast<const u32x4 *>(sb);
     r.q0 = *reinterpret_cast<const u32x4 *>(qs);
@@ -155,12 +229,11 @@ struct FmtQ4_K {
     r.q1 = r.h;
     return r;
   }
-  static __device__ __forceinline__ void stage_sums(float *sums, int idx, float slo, float shi) {
-    sums[2 * idx] = -1024.0f * slo;
-    sums[2 * idx + 1] = -1024.0f * shi;
+  static __device__ __forceinline__ uint32_t word(const Raw &r, int t) {
+    return t < 4 ? r.q0[t & 3] : r.q1[t & 3];
   }
 
-  // 6-bit scale and min of sub-block s from the scale words h1, h2, h3.
+  // 6-bit scale and min of sub-block s from the scale words h.y, h.z, h.w.
   static __device__ __forceinline__ void scale_min(const u32x4 &h, int s, uint32_t &sc,
                                                    uint32_t &m) {
     uint32_t sh = (s & 3) * 8;
@@ -172,10 +245,17 @@ struct FmtQ4_K {
     m = s < 4 ? m_lo : m_hi;
   }
 
+  // VALU mode. Staged sums per (unit, batch row): (-1024*S_lo, -1024*S_hi),
+  // which remove the 1024 bias of each dot product and give the activation
+  // sums the dmin * m term needs.
+  static __device__ __forceinline__ void stage_sums(float *sums, int idx, float slo, float shi) {
+    sums[2 * idx] = -1024.0f * slo;
+    sums[2 * idx + 1] = -1024.0f * shi;
+  }
   template <int B, int R>
   static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs,
-                                                 const float *sums, int u, int nu,
-                                                 float (&acc)[R][B]) {
+                                                 const float *sums, int u, int nu, bool valid,
+                                                 const UnpackMasks &k, float (&acc)[R][B]) {
     float slo[R][B], shi[R][B], nsl[B], nsh[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -194,8 +274,7 @@ struct FmtQ4_K {
       for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * nu + u];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        uint32_t w = t < 4 ? raw[r].q0[t & 3] : raw[r].q1[t & 3];
-        Nibbles n = unpack_word(w);
+        Nibbles n = unpack_word(word(raw[r], t), k);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           float lo = slo[r][b], hi = shi[r][b];
@@ -211,8 +290,8 @@ struct FmtQ4_K {
     const int pair = u & 3;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float d = f16_bits_to_f32(raw[r].h.x & 0xFFFF);
-      float dmin = f16_bits_to_f32(raw[r].h.x >> 16);
+      float d = valid ? f16_bits_to_f32(raw[r].h.x & 0xFFFF) : 0.0f;
+      float dmin = valid ? f16_bits_to_f32(raw[r].h.x >> 16) : 0.0f;
       uint32_t sc0, m0, sc1, m1;
       scale_min(raw[r].h, 2 * pair, sc0, m0);
       scale_min(raw[r].h, 2 * pair + 1, sc1, m1);
@@ -231,110 +310,547 @@ struct FmtQ4_K {
       }
     }
   }
+
+  // MFMA mode: fp16 weights d*sc*q - dmin*m with d*sc and dmin*m each
+  // rounded to fp16 once per sub-block, then one fused rounding per weight;
+  // valid == false yields zero weights.
+  static __device__ __forceinline__ Prep prep(const Raw &r, int pair, bool valid) {
+    float d = valid ? f16_bits_to_f32(r.h.x & 0xFFFF) : 0.0f;
+    float dmin = valid ? f16_bits_to_f32(r.h.x >> 16) : 0.0f;
+    uint32_t sc0, m0, sc1, m1;
+    scale_min(r.h, 2 * pair, sc0, m0);
+    scale_min(r.h, 2 * pair + 1, sc1, m1);
+    Prep p;
+    p.dsc_lo = h2(d * (float)sc0);
+    p.dmm_lo = h2(-dmin * (float)m0);
+    p.dsc_hi = h2(d * (float)sc1);
+    p.dmm_hi = h2(-dmin * (float)m1);
+    return p;
+  }
+  static __device__ __forceinline__ u32x4 dequant(const Raw &r, const Prep &p, int t,
+                                                 const UnpackMasks &k) {
+    Nibbles n = unpack_word(word(r, t), k);
+    const half2_t lo_bias = h2(-1024.0f), sixteenth = h2(0.0625f), hi_bias = h2(-64.0f);
+    u32x4 w;
+    w.x = as_u32(pk_fma(n.p0 + lo_bias, p.dsc_lo, p.dmm_lo));
+    w.y = as_u32(pk_fma(pk_fma(n.p1, sixteenth, hi_bias), p.dsc_hi, p.dmm_hi));
+    w.z = as_u32(pk_fma(n.p2 + lo_bias, p.dsc_lo, p.dmm_lo));
+    w.w = as_u32(pk_fma(pk_fma(n.p3, sixteenth, hi_bias), p.dsc_hi, p.dmm_hi));
+    return w;
+  }
+  // U consecutive units starting at `unit`; four units starting at a
+  // super-block boundary share one header load.
+  // A row holds a multiple of 4 units (last + 1 is a multiple of 4). For
+  // U == 4 the run is one whole super-block: its start is clamped to the
+  // last super-block, so every load stays inside the row.
+  template <int U>
+  static __device__ __forceinline__ void load_units(const uint8_t *row, uint32_t unit,
+                                                    uint32_t last, Raw (&out)[U]) {
+    if (U == 4) {
+      const uint32_t sbi = (unit >> 2) <= (last >> 2) ? (unit >> 2) : (last >> 2);
+      const uint8_t *sb = row + sbi * 144u;
+      const u32x4 h = *reinterpret_cast<const u32x4 *>(sb);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        out[j].h = h;
+        out[j].q0 = *reinterpret_cast<const u32x4 *>(sb + 16 + 32 * j);
+        out[j].q1 = *reinterpret_cast<const u32x4 *>(sb + 32 + 32 * j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < U; ++j) out[j] = load(row, unit + j <= last ? unit + j : last);
+    }
+  }
 };
 
-// ---- the kernel -------------------------------------------------------------
+// ---- activation staging ------------------------------------------------------
+// Word (b, u, t) holds the 8 activations of word t of unit u for batch row b,
+// in unpack order; `hi_scale` multiplies the hi values (1/16 in VALU mode so
+// that (1024 + 16q) * x/16 = 64x + qx, 1 in MFMA mode). `index(b, u, t)` gives
+// the word's LDS slot; consecutive threads write consecutive slots.
+template <class F>
+__device__ __forceinline__ u32x4 stage_word(const float *__restrict__ x, int64_t ldx, int b,
+                                            int u, int t, float hi_scale) {
+  const float *base = x + b * ldx + (int64_t)u * F::kUnitWeights + 4 * t;
+  float4_t lo = *reinterpret_cast<const float4_t *>(base);
+  float4_t hi = *reinterpret_cast<const float4_t *>(base + F::kUnitWeights / 2) * hi_scale;
+  u32x4 word;
+  word.x = pack_half2(lo.x, lo.z);
+  word.y = pack_half2(hi.x, hi.z);
+  word.z = pack_half2(lo.y, lo.w);
+  word.w = pack_half2(hi.y, hi.w);
+  return word;
+}
+
+// Sum of the lo (x, z halves) and hi (y, w halves) values of a staged word.
+__device__ __forceinline__ void word_sums(const u32x4 &w, float &slo, float &shi) {
+  half2_t a = as_half2(w.x), b = as_half2(w.y), c = as_half2(w.z), d = as_half2(w.w);
+  slo += ((float)a.x + (float)a.y) + ((float)c.x + (float)c.y);
+  shi += ((float)b.x + (float)b.y) + ((float)d.x + (float)d.y);
+}
+
+// ---- VALU-mode kernel -----------------------------------------------------
 // x rows: x + b*ldx, covering units [unit0, unit0 + nu) of every weight row.
 // accumulate != 0: y += result (used when K is split over several launches).
-template <class F, int B, int R>
+// A group is the slots*R rows one wave covers at once (slots = 64/LPR row
+// slots, R rows per lane).
+// FULL: all 64 lanes share each row (lpr_log2 == 6), so the rows a wave reads
+// are wave-uniform and their addresses live in scalar registers.
+template <class F, int B, int R, int U, bool FULL>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
             const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int64_t ldy,
-            int64_t N, int lpr_log2, int accumulate) {
+            int64_t N, int lpr_log2_arg, int accumulate) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int T = F::kWords;
   u32x4 *xs = reinterpret_cast<u32x4 *>(smem);
-  float *sums = reinterpret_cast<float *>(smem + (size_t)B * F::kWords * nu * 16);
+  float *sums = reinterpret_cast<float *>(smem + (size_t)B * T * nu * 16);
 
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int lpr_log2 = FULL ? 6 : lpr_log2_arg;
+  const int lpr = 1 << lpr_log2;
+  const int slot = FULL ? 0 : lane >> lpr_log2;
+  const int p = lane & (lpr - 1);
+  const int slots = kWave >> lpr_log2;
+  const int64_t rows_per_group = (int64_t)slots * R;
+  const int64_t ngroups = (N + rows_per_group - 1) / rows_per_group;
+  const int units_per_chunk = lpr * U;
+  const int nchunks = (nu + units_per_chunk - 1) / units_per_chunk;
+  const int64_t wave_stride = (int64_t)gridDim.x * kWavesPerWg;
 
-  // 1. stage activations: item (b, u, t) -> 8 fp16 values in unpack order.
-  {
-    constexpr int T = F::kWords;
-    constexpr int HALF = F::kUnitWeights / 2;
-    const int nitems = B * nu * T;
-    for (int i = tid; i < nitems; i += kGemvThreads) {
-      const int t = i % T;
-      const int bu = i / T;
-      const int u = bu % nu;
-      const int b = bu / nu;
-      const float *base = x + b * ldx + (int64_t)u * F::kUnitWeights + 4 * t;
-      float4_t lo = *reinterpret_cast<const float4_t *>(base);
-      float4_t hi = *reinterpret_cast<const float4_t *>(base + HALF) * 0.0625f;
-      half_t l0 = (half_t)lo.x, l1 = (half_t)lo.y, l2 = (half_t)lo.z, l3 = (half_t)lo.w;
-      half_t h0 = (half_t)hi.x, h1 = (half_t)hi.y, h2 = (half_t)hi.z, h3 = (half_t)hi.w;
-      u32x4 word;
-      word.x = as_u32(half2_t{l0, l2});
-      word.y = as_u32(half2_t{h0, h2});
-      word.z = as_u32(half2_t{l1, l3});
-      word.w = as_u32(half2_t{h1, h3});
-      xs[(b * T + t) * nu + u] = word;
-      float slo = ((float)l0 + (float)l1) + ((float)l2 + (float)l3);
-      float shi = ((float)h0 + (float)h1) + ((float)h2 + (float)h3);
-      slo = group_sum(slo, T);
-      shi = group_sum(shi, T);
-      if (t == T - 1) F::stage_sums(sums, b * nu + u, slo, shi);
+  // Loads are issued unconditionally from clamped (always valid) addresses:
+  // a conditional load would make the compiler wait for every outstanding
+  // load before using the current chunk, which serializes the prefetch.
+  // Rows past N are computed but never stored; units past nu are skipped.
+  typename F::Raw buf0[R][U], buf1[R][U];
+  auto load = [&](typename F::Raw (&dst)[R][U], int64_t g, int c) {
+    const int64_t row0 = g * rows_per_group + (int64_t)slot * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r < N ? row0 + r : N - 1;
+      const uint8_t *rowp = W + row * row_bytes + F::unit_offset(unit0);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        int u = c * units_per_chunk + j * lpr + p;
+        u = u < nu ? u : nu - 1;
+        dst[r][j] = F::load(rowp, (uint32_t)u);
+      }
     }
+  };
+
+  int64_t g = (int64_t)blockIdx.x * kWavesPerWg + __builtin_amdgcn_readfirstlane(tid / kWave);
+  int c = 0;
+  load(buf0, g < ngroups ? g : ngroups - 1, 0);
+
+  // Stage: slot (b*T + t)*nu + u, u fastest; then the per-(b, u) sums.
+  for (int i = tid; i < B * T * nu; i += kGemvThreads) {
+    const int u = i % nu, bt = i / nu;
+    xs[i] = stage_word<F>(x, ldx, bt / T, u, bt % T, 0.0625f);
+  }
+  __syncthreads();
+  for (int i = tid; i < B * nu; i += kGemvThreads) {
+    const int u = i % nu, b = i / nu;
+    float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) word_sums(xs[(b * T + t) * nu + u], slo, shi);
+    F::stage_sums(sums, i, slo, shi);
   }
   __syncthreads();
 
-  // 2. rows.
-  const int lane = tid & (kWave - 1);
-  const int lpr = 1 << lpr_log2;
-  const int slot = lane >> lpr_log2;
-  const int p = lane & (lpr - 1);
-  const int slots = kWave >> lpr_log2;
-  const int64_t rows_per_iter = (int64_t)slots * R;
-  const int64_t wave = (int64_t)blockIdx.x * (kGemvThreads / kWave) + (tid / kWave);
-  const int64_t nwaves = (int64_t)gridDim.x * (kGemvThreads / kWave);
+  const UnpackMasks kmask;
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
-  for (int64_t rowbase = wave * rows_per_iter; rowbase < N; rowbase += nwaves * rows_per_iter) {
-    const int64_t row0 = rowbase + (int64_t)slot * R;
-    float acc[R][B];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
-    for (int u = p; u < nu; u += lpr) {
-      typename F::Raw raw[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int64_t row = row0 + r;
-        raw[r] = row < N ? F::load(W + row * row_bytes, unit0 + u) : F::zero();
-      }
-      F::template compute<B, R>(raw, xs, sums, u, nu, acc);
+  // Compute chunk (g, c) from src while the next chunk loads into dst.
+  auto stage = [&](typename F::Raw (&src)[R][U], typename F::Raw (&dst)[R][U]) -> bool {
+    int64_t g2 = g;
+    int c2 = c + 1;
+    if (c2 == nchunks) {
+      c2 = 0;
+      g2 += wave_stride;
     }
-
+    // past the last group: reload the current chunk (an L2 hit) so the
+    // load stays unconditional
+    load(dst, g2 < ngroups ? g2 : g, g2 < ngroups ? c2 : c);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int j = 0; j < U; ++j) {
+      const int u = c * units_per_chunk + j * lpr + p;
+      typename F::Raw one[R];
 #pragma unroll
-      for (int b = 0; b < B; ++b) acc[r][b] = group_sum(acc[r][b], lpr);
-
-    if (p == lpr - 1) {
+      for (int r = 0; r < R; ++r) one[r] = src[r][j];
+      F::template compute<B, R>(one, xs, sums, u < nu ? u : nu - 1, nu, u < nu, kmask, acc);
+    }
+    if (c == nchunks - 1) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int64_t row = row0 + r;
-        if (row < N) {
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int b = 0; b < B; ++b) {
-            float v = acc[r][b];
-            if (accumulate) v += y[b * ldy + row];
-            y[b * ldy + row] = v;
+        for (int b = 0; b < B; ++b) acc[r][b] = group_sum(acc[r][b], lpr);
+      if (p == lpr - 1) {
+        const int64_t row0 = g * rows_per_group + (int64_t)slot * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t row = row0 + r;
+          if (row < N) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+              float v = acc[r][b];
+              if (accumulate) v += y[b * ldy + row];
+              y[b * ldy + row] = v;
+            }
           }
         }
       }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    }
+    g = g2;
+    c = c2;
+    return g < ngroups;
+  };
+
+  if (g < ngroups) {
+    while (stage(buf0, buf1) && stage(buf1, buf0)) {
     }
   }
 }
 
-template <class F, int B, int R>
-hipError_t launch_one(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
-                      hipStream_t stream) {
-  auto kern = gemv_kernel<F, B, R>;
+// ---- MFMA-mode kernel -----------------------------------------------------
+// nb (1..16) batch rows. A "tile" is 16 weight rows. The KS waves of a
+// k-split team share R tiles: wave slice s takes units [s*nus, (s+1)*nus) of
+// every row (nus = units per slice), and the team's partial sums meet in LDS.
+// Within a slice, lane l takes weight row l % 16 of each tile and, in chunk c,
+// the U consecutive units c*4U + (l/16)*U + j (j < U), so every row is read in
+// runs of 4U units. The lane's activations (A operand) are those of batch row
+// l % 16 for the same unit; lanes with l % 16 >= nb feed zeros. The result
+// D[4*(l/16) + v][l % 16] is batch row 4*(l/16) + v of weight row l % 16.
+// The 8/KS teams of a workgroup walk tile groups with a grid stride; every
+// wave of the workgroup runs the same number of iterations, so the team
+// reduction can use workgroup barriers.
+template <class F, int R, int U, int KS, int NW>
+__global__ void __launch_bounds__(NW * kWave)
+gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
+                 const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int64_t ldy,
+                 int64_t N, int nb, int accumulate) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int T = F::kWords;
+  constexpr int kThreads = NW * kWave;
+  constexpr int kTeams = NW / KS;
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (t*nu + u)*nb + b
+  float4_t *red = reinterpret_cast<float4_t *>(smem + (size_t)nb * T * nu * 16);
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int team = wave / KS, slice = wave % KS;
+  const int lane = tid & (kWave - 1);
+  const int n = lane & 15;   // weight row within a tile; batch row of the A operand
+  const int q = lane >> 4;   // k group of the MFMA operands
+  const int64_t rows_per_group = 16 * R;
+  const int64_t ngroups = (N + rows_per_group - 1) / rows_per_group;
+  const int units_per_chunk = 4 * U;
+  // Units per slice, a whole number of chunks; every slice runs the same
+  // number of chunks (units past the end feed zero activations).
+  const int nus = (((nu + KS - 1) / KS) + units_per_chunk - 1) / units_per_chunk * units_per_chunk;
+  const int ubeg = slice * nus;
+  const int uend = ubeg + nus < nu ? ubeg + nus : nu;
+  const int nchunks = nus / units_per_chunk;
+  const int64_t group_stride = (int64_t)gridDim.x * kTeams;
+
+  // First unit of the run lane group q loads in chunk c: the nominal start,
+  // moved back so that the run ends at nu when it would run past it (never
+  // below 0; shorter rows are handled by the per-unit clamp in load_units).
+  auto run_start = [&](int c) -> int {
+    const int u = ubeg + c * units_per_chunk + q * U;
+    if (u + U <= nu) return u;
+    return nu - U > 0 ? nu - U : 0;
+  };
+
+  // Unconditional loads from clamped addresses (see the VALU kernel).
+  typename F::Raw buf0[R][U], buf1[R][U];
+  auto load = [&](typename F::Raw (&dst)[R][U], int64_t gg, int c) {
+    const int64_t gc = gg < ngroups ? gg : ngroups - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t row = gc * rows_per_group + 16 * r + n;
+      row = row < N ? row : N - 1;
+      const uint8_t *rowp = W + row * row_bytes + F::unit_offset(unit0);
+      // The U units of a lane are consecutive: the run is moved back to end
+      // at nu, and each unit is also clamped for rows shorter than a run.
+      F::template load_units<U>(rowp, (uint32_t)run_start(c), (uint32_t)(nu - 1), dst[r]);
+    }
+  };
+
+  // All waves of the workgroup walk the same sequence of group steps; a
+  // team whose group is past the end computes on clamped data and stores
+  // nothing.
+  int64_t gb = (int64_t)blockIdx.x * kTeams;  // first group of this workgroup
+  int c = 0;
+  load(buf0, gb + team, 0);
+
+  for (int i = tid; i < nb * T * nu; i += kThreads) {
+    const int b = i % nb, tu = i / nb;
+    xs[i] = stage_word<F>(x, ldx, b, tu % nu, tu / nu, 1.0f);
+  }
+  __syncthreads();
+
+  const UnpackMasks kmask;
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0, 0, 0, 0};
+
+  auto stage = [&](typename F::Raw (&src)[R][U], typename F::Raw (&dst)[R][U]) -> bool {
+    int64_t gb2 = gb;
+    int c2 = c + 1;
+    if (c2 == nchunks) {
+      c2 = 0;
+      gb2 += group_stride;
+    }
+    load(dst, (gb2 < ngroups ? gb2 : gb) + team, gb2 < ngroups ? c2 : c);
+    // The loader clamped the run to [nu - U, nu); recover which units were
+    // actually loaded so the activations match, and zero the weights of
+    // units outside this slice.
+    const int ufirst = ubeg + c * units_per_chunk + q * U;
+    const int uload = run_start(c);
+    const int xb = n < nb ? n : 0;  // rows >= nb are computed but never stored
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = uload + j;
+      const bool valid = u >= ufirst && u < uend;
+      const int ux = u < nu ? u : nu - 1;  // the unit load_units fetched
+      const u32x4 *xrow = xs + (int64_t)ux * nb + xb;
+      typename F::Prep pr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) pr[r] = F::prep(src[r][j], ux & 3, valid);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const half8_t a = __builtin_bit_cast(half8_t, xrow[t * nu * nb]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(src[r][j], pr[r], t, kmask));
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wv, acc[r], 0, 0, 0);
+        }
+      }
+    }
+    if (c == nchunks - 1) {
+      // team reduction in LDS, stored by the slice-0 wave
+      if (KS > 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) red[(wave * R + r) * kWave + lane] = acc[r];
+        __syncthreads();
+        if (slice == 0) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s2 = 1; s2 < KS; ++s2) acc[r] += red[((wave + s2) * R + r) * kWave + lane];
+        }
+      }
+      const int64_t g = gb + team;
+      if (slice == 0 && g < ngroups) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t row = g * rows_per_group + 16 * r + n;
+          if (row < N) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int b = 4 * q + v;
+              if (b < nb) {
+                float val = acc[r][v];
+                if (accumulate) val += y[b * ldy + row];
+                y[b * ldy + row] = val;
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = float4_t{0, 0, 0, 0};
+      if (KS > 1) __syncthreads();
+    }
+    gb = gb2;
+    c = c2;
+    return gb < ngroups;
+  };
+
+  if (gb < ngroups) {
+    while (stage(buf0, buf1) && stage(buf1, buf0)) {
+    }
+  }
+}
+
+// ---- Q4_K MFMA mode with coalesced loads --------------------------------------
+// Same decomposition as gemv_mfma_kernel (tiles of 16 rows, KS k-slices per
+// team), but a chunk is U whole super-blocks of each of the 16 rows, and it
+// is fetched with coalesced loads: piece p (16 bytes) of the chunk goes to
+// lane p % 64 of load p / 64, so consecutive lanes read consecutive bytes of
+// a row. The pieces are written to a wave-private LDS buffer and read back in
+// the MFMA B-operand layout (lane l: row l % 16, units (l/16)*U .. +U-1).
+// The MFMA-layout loads of gemv_mfma_kernel touch 16 rows per instruction and
+// keep the L1 address path stalled; these touch one to four rows.
+// D chunks are kept in flight per wave through a ring of D register buffers
+// (chunk i is consumed from buffer i % D, which then receives chunk i + D).
+template <int U, int KS, int D>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_q4k_lds_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
+                    const float *__restrict__ x, int64_t ldx, float *__restrict__ y,
+                    int64_t ldy, int64_t N, int nb, int accumulate) {
+  using F = FmtQ4_K;
+  constexpr int NW = kWavesPerWg;
+  constexpr int T = F::kWords;
+  constexpr int kTeams = NW / KS;
+  constexpr int PR = 9 * U;             // 16-byte pieces per row per chunk
+  constexpr int NP = 16 * PR;           // pieces per chunk
+  constexpr int NI = (NP + 63) / 64;    // loads per lane per chunk
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (t*nu + u)*nb + b
+  float4_t *red = reinterpret_cast<float4_t *>(smem + (size_t)nb * T * nu * 16);
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int team = wave / KS, slice = wave % KS;
+  const int lane = tid & (kWave - 1);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+  u32x4 *wbuf = reinterpret_cast<u32x4 *>(smem + (size_t)nb * T * nu * 16 + NW * kWave * 16) +
+                wave * NI * kWave;
+  const int64_t ngroups = (N + 15) / 16;
+  const int units_per_chunk = 4 * U;
+  const int nus = (((nu + KS - 1) / KS) + units_per_chunk - 1) / units_per_chunk * units_per_chunk;
+  const int ubeg = slice * nus;
+  const int uend = ubeg + nus < nu ? ubeg + nus : nu;
+  const int nchunks = nus / units_per_chunk;
+  const int64_t group_stride = (int64_t)gridDim.x * kTeams;
+
+  // First unit of chunk c, moved back so the chunk ends inside the row
+  // (nu is a multiple of 4U here).
+  auto chunk_start = [&](int c) -> int {
+    const int u = ubeg + c * units_per_chunk;
+    return u + units_per_chunk <= nu ? u : nu - units_per_chunk;
+  };
+
+  // Chunk c of group gg (clamped to the last group) into dst.
+  auto load = [&](u32x4 (&dst)[NI], int64_t gg, int c) {
+    const int64_t gc = gg < ngroups ? gg : ngroups - 1;
+    const int64_t sb0 = (unit0 + chunk_start(c)) >> 2;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      int pc = k * kWave + lane;
+      pc = pc < NP ? pc : NP - 1;
+      int64_t row = gc * 16 + pc / PR;
+      row = row < N ? row : N - 1;
+      dst[k] = *reinterpret_cast<const u32x4 *>(W + row * row_bytes + sb0 * 144 + (pc % PR) * 16);
+    }
+  };
+
+  u32x4 bufs[D][NI];
+  const int64_t gbase = (int64_t)blockIdx.x * kTeams;  // first group of this workgroup
+  // Item i of this wave: chunk i % nchunks of group gbase + (i / nchunks) *
+  // group_stride + team. The workgroup loops while that group index (without
+  // the team) is below ngroups, so all its waves run the same iterations.
+  auto item_gb = [&](int64_t i) { return gbase + (i / nchunks) * group_stride; };
+  auto load_item = [&](u32x4 (&dst)[NI], int64_t i) {
+    load(dst, item_gb(i) + team, (int)(i % nchunks));
+  };
+#pragma unroll
+  for (int k = 0; k < D; ++k) load_item(bufs[k], k);
+
+  for (int i = tid; i < nb * T * nu; i += kGemvThreads) {
+    const int b = i % nb, tu = i / nb;
+    xs[i] = stage_word<F>(x, ldx, b, tu % nu, tu / nu, 1.0f);
+  }
+  __syncthreads();
+
+  const UnpackMasks kmask;
+  float4_t acc = float4_t{0, 0, 0, 0};
+  const int xb = n < nb ? n : 0;
+
+  // Consume buffer `src` (item i), then refill it with item i + D.
+  auto stage = [&](u32x4 (&src)[NI], int64_t i) {
+    const int c = (int)(i % nchunks);
+    const int64_t gb = item_gb(i);
+    // Wave-private transpose through LDS; one wave's LDS operations complete
+    // in order, so the reads below see these writes.
+#pragma unroll
+    for (int k = 0; k < NI; ++k) wbuf[k * kWave + lane] = src[k];
+    load_item(src, i + D);
+    const int nominal = ubeg + c * units_per_chunk;
+    const int ustart = chunk_start(c);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int ul = q * U + j;               // unit within the chunk
+      const int u = ustart + ul;
+      const bool valid = u >= nominal && u < uend;
+      const u32x4 *pb = wbuf + n * PR + (ul >> 2) * 9;
+      F::Raw r;
+      r.h = pb[0];
+      r.q0 = pb[1 + 2 * (ul & 3)];
+      r.q1 = pb[2 + 2 * (ul & 3)];
+      const F::Prep pr = F::prep(r, ul & 3, valid);
+      const u32x4 *xrow = xs + (int64_t)u * nb + xb;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const half8_t a = __builtin_bit_cast(half8_t, xrow[t * nu * nb]);
+        const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(r, pr, t, kmask));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wv, acc, 0, 0, 0);
+      }
+    }
+    if (c == nchunks - 1) {
+      if (KS > 1) {
+        red[wave * kWave + lane] = acc;
+        __syncthreads();
+        if (slice == 0) {
+#pragma unroll
+          for (int s2 = 1; s2 < KS; ++s2) acc += red[(wave + s2) * kWave + lane];
+        }
+      }
+      const int64_t g = gb + team;
+      if (slice == 0 && g < ngroups) {
+        const int64_t row = g * 16 + n;
+        if (row < N) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int b = 4 * q + v;
+            if (b < nb) {
+              float val = acc[v];
+              if (accumulate) val += y[b * ldy + row];
+              y[b * ldy + row] = val;
+            }
+          }
+        }
+      }
+      acc = float4_t{0, 0, 0, 0};
+      if (KS > 1) __syncthreads();
+    }
+  };
+
+  int64_t i = 0;
+  while (item_gb(i) < ngroups) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      stage(bufs[k], i);
+      ++i;
+      if (item_gb(i) >= ngroups) break;
+    }
+  }
+}
+
+template <class K>
+hipError_t set_lds_attr(K kern) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kMaxGemvLds);
+}
+
+template <class F, int B, int R, int U, bool FULL>
+hipError_t launch_valu(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                       hipStream_t stream) {
+  auto kern = gemv_kernel<F, B, R, U, FULL>;
   static bool attr_done = false;  // benign race: setting the attribute twice is harmless
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxGemvLds);
+    hipError_t e = set_lds_attr(kern);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
@@ -344,37 +860,111 @@ hipError_t launch_one(const GemvPlan &pl, const uint8_t *W, const float *x, floa
   return hipGetLastError();
 }
 
-template <class F, int B>
-hipError_t launch_r(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
-                    hipStream_t s) {
-  switch (pl.rows_per_lane) {
-    case 1: return launch_one<F, B, 1>(pl, W, x, y, s);
-    case 2: return launch_one<F, B, 2>(pl, W, x, y, s);
-    default: return launch_one<F, B, 4>(pl, W, x, y, s);
+template <int U, int KS, int D>
+hipError_t launch_q4k_lds(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                          hipStream_t stream) {
+  auto kern = gemv_q4k_lds_kernel<U, KS, D>;
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_done = true;
   }
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, stream, W,
+                     pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
+                     pl.accumulate);
+  return hipGetLastError();
+}
+
+template <class F, int R, int U, int KS, int NW>
+hipError_t launch_mfma(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                       hipStream_t stream) {
+  auto kern = gemv_mfma_kernel<F, R, U, KS, NW>;
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = set_lds_attr(kern);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(NW * kWave), pl.lds_bytes, stream, W,
+                     pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
+                     pl.accumulate);
+  return hipGetLastError();
+}
+
+// (rows per lane, units per lane per chunk) shapes that are instantiated.
+template <class F, int B, bool FULL>
+hipError_t launch_ru(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                     hipStream_t s) {
+  const int r = pl.rows_per_lane, u = pl.units_per_lane;
+  if (r == 1 && u == 4) return launch_valu<F, B, 1, 4, FULL>(pl, W, x, y, s);
+  if (r == 1) return launch_valu<F, B, 1, 2, FULL>(pl, W, x, y, s);
+  if (r == 2 && u == 1) return launch_valu<F, B, 2, 1, FULL>(pl, W, x, y, s);
+  return launch_valu<F, B, 2, 2, FULL>(pl, W, x, y, s);
 }
 
 template <class F>
-hipError_t launch_b(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
-                    hipStream_t s) {
-  switch (pl.batch) {
-    case 1: return launch_r<F, 1>(pl, W, x, y, s);
-    case 2: return launch_r<F, 2>(pl, W, x, y, s);
-    case 3: return launch_r<F, 3>(pl, W, x, y, s);
-    case 4: return launch_r<F, 4>(pl, W, x, y, s);
-    case 5: return launch_r<F, 5>(pl, W, x, y, s);
-    case 6: return launch_r<F, 6>(pl, W, x, y, s);
-    case 7: return launch_r<F, 7>(pl, W, x, y, s);
-    default: return launch_r<F, 8>(pl, W, x, y, s);
+hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                      hipStream_t s) {
+  if (pl.mfma) {
+    const int u = pl.units_per_lane;
+    if (pl.lds_stage) {
+#define LQMM_Q4K_LDS(UU, DD)                                                  \
+  switch (pl.ksplit) {                                                       \
+    case 1: return launch_q4k_lds<UU, 1, DD>(pl, W, x, y, s);                \
+    case 2: return launch_q4k_lds<UU, 2, DD>(pl, W, x, y, s);                \
+    case 4: return launch_q4k_lds<UU, 4, DD>(pl, W, x, y, s);                \
+    default: return launch_q4k_lds<UU, 8, DD>(pl, W, x, y, s);               \
   }
+      if (u == 2) {
+        if (pl.depth >= 3) { LQMM_Q4K_LDS(2, 3) }
+        LQMM_Q4K_LDS(2, 2)
+      }
+      if (pl.depth >= 6) { LQMM_Q4K_LDS(1, 6) }
+      if (pl.depth >= 4) { LQMM_Q4K_LDS(1, 4) }
+      LQMM_Q4K_LDS(1, 2)
+#undef LQMM_Q4K_LDS
+    }
+    if (pl.waves == 16) {
+      switch (pl.ksplit) {
+        case 4: return u == 4 ? launch_mfma<F, 1, 4, 4, 16>(pl, W, x, y, s)
+                              : launch_mfma<F, 1, 2, 4, 16>(pl, W, x, y, s);
+        case 8: return u == 4 ? launch_mfma<F, 1, 4, 8, 16>(pl, W, x, y, s)
+                              : launch_mfma<F, 1, 2, 8, 16>(pl, W, x, y, s);
+        default: return u == 4 ? launch_mfma<F, 1, 4, 16, 16>(pl, W, x, y, s)
+                               : launch_mfma<F, 1, 2, 16, 16>(pl, W, x, y, s);
+      }
+    }
+    switch (pl.ksplit) {
+      case 1: return u == 4 ? launch_mfma<F, 1, 4, 1, 8>(pl, W, x, y, s)
+                            : launch_mfma<F, 1, 2, 1, 8>(pl, W, x, y, s);
+      case 2: return u == 4 ? launch_mfma<F, 1, 4, 2, 8>(pl, W, x, y, s)
+                            : launch_mfma<F, 1, 2, 2, 8>(pl, W, x, y, s);
+      case 4: return u == 4 ? launch_mfma<F, 1, 4, 4, 8>(pl, W, x, y, s)
+                            : launch_mfma<F, 1, 2, 4, 8>(pl, W, x, y, s);
+      default: return u == 4 ? launch_mfma<F, 1, 4, 8, 8>(pl, W, x, y, s)
+                             : launch_mfma<F, 1, 2, 8, 8>(pl, W, x, y, s);
+    }
+  }
+  const bool full = pl.lpr_log2 == 6;
+  if (pl.batch == 1)
+    return full ? launch_ru<F, 1, true>(pl, W, x, y, s) : launch_ru<F, 1, false>(pl, W, x, y, s);
+  return full ? launch_ru<F, 2, true>(pl, W, x, y, s) : launch_ru<F, 2, false>(pl, W, x, y, s);
 }
 
 }  // namespace
 
-size_t gemv_lds_bytes(GemvFormat f, int batch, int nu) {
-  if (f == GemvFormat::Q4_0)
-    return (size_t)batch * nu * (FmtQ4_0::kWords * 16 + FmtQ4_0::kSums * 4);
-  return (size_t)batch * nu * (FmtQ4_K::kWords * 16 + FmtQ4_K::kSums * 4);
+size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu) {
+  const int words = f == GemvFormat::Q4_0 ? FmtQ4_0::kWords : FmtQ4_K::kWords;
+  const int sums = f == GemvFormat::Q4_0 ? FmtQ4_0::kSums : FmtQ4_K::kSums;
+  return (size_t)batch * nu * (words * 16 + (mfma ? 0 : sums * 4));
+}
+
+size_t gemv_mfma_reduce_bytes(int waves) { return (size_t)waves * kWave * 16; }
+
+size_t gemv_q4k_lds_stage_bytes(int u) {
+  return (size_t)kWavesPerWg * ((16 * 9 * u + 63) / 64) * kWave * 16;
 }
 
 int gemv_unit_weights(GemvFormat f) {
@@ -385,8 +975,8 @@ int gemv_threads() { return kGemvThreads; }
 
 hipError_t gemv_launch(GemvFormat f, const GemvPlan &pl, const uint8_t *W, const float *x,
                        float *y, hipStream_t stream) {
-  if (f == GemvFormat::Q4_0) return launch_b<FmtQ4_0>(pl, W, x, y, stream);
-  return launch_b<FmtQ4_K>(pl, W, x, y, stream);
+  if (f == GemvFormat::Q4_0) return launch_fmt<FmtQ4_0>(pl, W, x, y, stream);
+  return launch_fmt<FmtQ4_K>(pl, W, x, y, stream);
 }
 
 }  // namespace lqmm

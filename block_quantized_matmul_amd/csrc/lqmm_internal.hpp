@@ -15,8 +15,14 @@ enum class GemvFormat { Q4_0, Q4_K };
 constexpr int kMaxGemvLds = 144 * 1024;
 
 struct GemvPlan {
-  int batch;          // activation rows in this launch, 1..8
+  int mfma;           // 1: matrix-core mode (batch up to 16), 0: VALU dot2 mode (batch 1 or 2)
+  int batch;          // activation rows in this launch
   int rows_per_lane;  // 1, 2 or 4
+  int units_per_lane; // units each lane loads per chunk: VALU (R, U) in {(1,2),(1,4),(2,1),(2,2)}
+  int ksplit;         // MFMA mode: waves sharing one tile along K (1..8; 4..16 with 16 waves)
+  int waves;          // MFMA mode: waves per workgroup (8 or 16)
+  int lds_stage;      // MFMA mode, Q4_K: coalesced loads staged through LDS (8 waves)
+  int depth;          // lds_stage: chunks in flight per wave (2, 4 or 6 with U = 1; 2 or 3 with U = 2)
   int lpr_log2;       // log2(lanes sharing one weight row)
   int nu;             // units (of gemv_unit_weights weights) per row in this launch
   int64_t unit0;      // first unit of each row covered by this launch
@@ -28,7 +34,10 @@ struct GemvPlan {
   int accumulate;     // 1: y += result
 };
 
-size_t gemv_lds_bytes(GemvFormat f, int batch, int nu);
+size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu);
+size_t gemv_mfma_reduce_bytes(int waves);  // extra LDS of an MFMA-mode launch
+size_t gemv_q4k_lds_stage_bytes(int u);     // per-workgroup staging of the coalesced Q4_K kernel
+constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 int gemv_unit_weights(GemvFormat f);
 int gemv_threads();
 hipError_t gemv_launch(GemvFormat f, const GemvPlan &plan, const uint8_t *W, const float *x,

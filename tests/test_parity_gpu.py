@@ -39,7 +39,8 @@ def _run_q4_k(c):
 # ----------------------------------------------------------------- Q4_0 GEMV
 Q4_0_SMALL = [(1, 32, 1), (7, 32, 3), (5, 64, 2), (13, 96, 1), (33, 288, 5), (64, 1024, 8),
               (100, 4096, 4), (1, 4096, 9), (3, 9216, 8), (257, 2048, 16), (2, 160, 7),
-              (1000, 512, 1), (31, 8192, 2)]
+              (1000, 512, 1), (31, 8192, 2), (17, 1024, 17), (40, 18432, 18), (129, 4096, 3),
+              (16, 512, 16), (3, 36864, 3)]
 
 
 @pytest.mark.parametrize("N,K,B", Q4_0_SMALL)
@@ -64,17 +65,23 @@ def test_q4_0_configs(orc, name):
 
 
 def test_q4_0_one_hot_exact(orc):
-    """One-hot activations extract weight columns exactly (x = 1 is exact in
-    fp16 and every partial sum is an exact small integer)."""
+    """One-hot activations extract weight columns. dot2 path (batch <= 2):
+    bit-exact (x = 1 is exact in fp16 and every partial sum is an exact small
+    integer). Matrix-core path (batch >= 3): the weight is rounded once to
+    fp16, so the result is exactly the fp16-rounded column."""
     c = synth.make("q4_0_gemv_1024")
     ks = [0, 1, 15, 16, 17, 31, 32, 500, 1007, 1023]
     x = np.zeros((len(ks), c.K), np.float32)
     for i, k in enumerate(ks):
         x[i, k] = 1.0
     announce("q4_0 one-hot exactness")
-    y = host(bq.lqmm_gemv_q4_0(dev(c.W.reshape(-1)), dev(x), c.N))
+    W = dev(c.W.reshape(-1))
     ref = orc.gemv_q4_0(c.W, x, c.N, c.K)
-    assert np.array_equal(y, ref.astype(np.float32))
+    for i in range(0, len(ks), 2):
+        y = host(bq.lqmm_gemv_q4_0(W, dev(x[i:i + 2]), c.N))
+        assert np.array_equal(y, ref[i:i + 2].astype(np.float32))
+    y = host(bq.lqmm_gemv_q4_0(W, dev(x), c.N))
+    assert np.array_equal(y, ref.astype(np.float16).astype(np.float32))
 
 
 def test_q4_0_subnormal_scales(orc):
@@ -86,21 +93,39 @@ def test_q4_0_subnormal_scales(orc):
     W = synth.pack_q4_0(d, q)
     x = np.eye(K, dtype=np.float32)[[0, 20, 77, 255]]
     announce("q4_0 subnormal scales")
-    y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x), N))
     ref = orc.gemv_q4_0(W, x, N, K)
-    assert np.array_equal(y, ref.astype(np.float32))
+    for i in (0, 2):   # dot2 path: exact
+        y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x[i:i + 2]), N))
+        assert np.array_equal(y, ref[i:i + 2].astype(np.float32))
+    y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x), N))  # matrix cores
+    assert np.array_equal(y, ref.astype(np.float16).astype(np.float32))
     xr = rng.standard_normal((2, K)).astype(np.float32)
     y2 = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(xr), N))
     assert_close(y2, orc.gemv_q4_0(W, xr, N, K), TOL_QUANT, "subnormal random x")
 
 
-def test_q4_0_batch_rows_match_single(orc):
-    c = synth.q4_0_case(300, 4096, 4, seed=9)
-    announce("q4_0 batch consistency")
-    yb = _run_q4_0(c)
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_k"])
+def test_batch_rows_are_independent(orc, fmt):
+    """Each output row depends only on its own activation row: within the dot2
+    path (batch <= 2) and within the matrix-core path (batch >= 3) a row's
+    result is bitwise the same whatever the other rows hold; across the two
+    paths results agree within the parity tolerance."""
+    if fmt == "q4_0":
+        c, fn = synth.q4_0_case(300, 4096, 4, seed=9), bq.lqmm_gemv_q4_0
+    else:
+        c, fn = synth.q4_k_case(300, 4096, 4, seed=9), bq.lqmm_gemv_q4_k
+    announce(f"{fmt} batch row independence")
+    W = dev(c.W.reshape(-1))
+    y4 = host(fn(W, dev(c.x), c.N))            # matrix cores
+    y2 = host(fn(W, dev(c.x[:2]), c.N))        # dot2
     for b in range(4):
-        y1 = host(bq.lqmm_gemv_q4_0(dev(c.W.reshape(-1)), dev(c.x[b]), c.N))
-        assert_close(y1, yb[b], (1e-6, 1e-6), f"row {b}")
+        y1 = host(fn(W, dev(c.x[b]), c.N))     # dot2, batch 1
+        if b < 2:
+            assert np.array_equal(y1, y2[b])
+        rep = np.repeat(c.x[b:b + 1], 3, axis=0)
+        y3 = host(fn(W, dev(rep), c.N))        # matrix cores, other rows equal
+        assert np.array_equal(y3[0], y4[b]) and np.array_equal(y3[2], y4[b])
+        assert_close(y4[b], y1, TOL_QUANT, f"row {b} across paths")
 
 
 def test_q4_0_deterministic():
@@ -114,7 +139,8 @@ def test_q4_0_deterministic():
 
 # ----------------------------------------------------------------- Q4_K GEMV
 Q4_K_SMALL = [(1, 256, 1), (3, 512, 2), (17, 768, 8), (5, 256, 9), (9, 8704, 8),
-              (70, 2048, 3), (129, 4096, 5), (2, 1280, 4), (40, 16384, 1), (257, 256, 6)]
+              (70, 2048, 3), (129, 4096, 5), (2, 1280, 4), (40, 16384, 1), (257, 256, 6),
+              (33, 4608, 16), (18, 2048, 19), (48, 18432, 12)]
 
 
 @pytest.mark.parametrize("N,K,B", Q4_K_SMALL)
@@ -136,15 +162,28 @@ def test_q4_k_configs(orc, name):
 
 
 def test_q4_k_one_hot_exact(orc):
+    """dot2 path (batch <= 2): one-hot columns are bit-exact. Matrix-core
+    path: d*sc, dmin*m and the weight d*sc*q - dmin*m are each rounded to fp16
+    once (round to nearest, relative error <= 2^-11 each), so every entry obeys
+    |err| <= 2^-11 (|d sc q| + |dmin m| + |w|) + 2^-24 (fp16 subnormal step)."""
     c = synth.q4_k_case(300, 2048, 1, seed=31)
     ks = [0, 31, 32, 63, 64, 200, 255, 256, 1500, 2047]
     x = np.zeros((len(ks), c.K), np.float32)
     for i, k in enumerate(ks):
         x[i, k] = 1.0
     announce("q4_k one-hot exactness")
-    y = host(bq.lqmm_gemv_q4_k(dev(c.W.reshape(-1)), dev(x[:8]), c.N))
-    ref = orc.gemv_q4_k(c.W, x[:8], c.N, c.K)
-    assert np.array_equal(y, ref.astype(np.float32))
+    W = dev(c.W.reshape(-1))
+    ref = orc.gemv_q4_k(c.W, x, c.N, c.K)
+    for i in range(0, len(ks), 2):
+        y = host(bq.lqmm_gemv_q4_k(W, dev(x[i:i + 2]), c.N))
+        assert np.array_equal(y, ref[i:i + 2].astype(np.float32))
+    y = host(bq.lqmm_gemv_q4_k(W, dev(x), c.N)).astype(np.float64)
+    for i, k in enumerate(ks):
+        sb, s = k // 256, (k % 256) // 32
+        a = np.abs(c.d[:, sb].astype(np.float64) * c.sc[:, sb, s] * c.q[:, k])
+        m = np.abs(c.dmin[:, sb].astype(np.float64) * c.m[:, sb, s])
+        bound = 2.0 ** -11 * (a + m + np.abs(ref[i])) * 1.001 + 2.0 ** -24
+        assert np.all(np.abs(y[i] - ref[i]) <= bound), k
 
 
 def test_q4_k_extreme_codes(orc):
