@@ -13,12 +13,15 @@ Weights rotate over enough device copies (>= 512 MiB per weight set, twice the
 
 Reported (one JSON line on stdout):
   value          quantized-GEMV effective HBM bandwidth: algorithmic bytes of
-                 the step's GEMV launches / their summed kernel time (GB/s);
+                 the step's GEMV launches / the GEMV share of the timed steps
+                 (GB/s); every share is timed with HIP events on the launch
+                 stream around HIP-graph segments of the step;
   roofline       the largest decode GEMV (Q4_K 28672 x 8192, batch 1) against
-                 the 8 TB/s HBM peak, timed with HIP events on the launch
-                 stream; traffic from the committed rocprofv3 counter summary;
+                 the 8 TB/s HBM peak, timed the same way inside the steps;
+                 traffic from the committed rocprofv3 counter summary;
   prefill_gemm   Q8_0 x fp16 GEMM TFLOP/s against the 2.5 PFLOP/s f16 peak;
-  cases          every call: kernel time, GB/s or TFLOP/s, roofline fraction;
+  fp32_gemm      fp32 GEMM TFLOP/s against the 157.3 TFLOP/s fp32 peak;
+  cases          every call timed alone: kernel time, GB/s or TFLOP/s;
   cpu_baseline   the fp64 CPU oracle on the same GEMV inputs (host cores).
 
 Algorithmic bytes count the packed weights, the activations and the outputs,
@@ -51,11 +54,18 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--reps", type=int, default=50, help="launches per case for per-kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--cases", default="", help="comma-separated subset of case names")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="wall time of the CPU-oracle baseline sample (whole passes)")
+    p.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "OUT_MD", "COMMAND", "TITLE"),
+                   help="host only: write a markdown summary of a rocprofv3 kernel_stats.csv")
+    p.add_argument("--summarize-traffic", nargs=5,
+                   metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_MIB", "CMD_FETCH", "CMD_WRITE"),
+                   help="host only: write the roofline kernel's HBM traffic summary from two "
+                        "rocprofv3 --pmc counter_collection.csv files")
     p.add_argument("--eager", action="store_true",
                    help="launch from Python one call at a time instead of replaying HIP graphs")
     return p.parse_args()
@@ -200,30 +210,6 @@ def capture(torch, fn):
     return g
 
 
-def time_case(torch, c, reps, warm, use_graph):
-    """Average duration of one launch over `reps` back-to-back launches
-    (rotating weight copies), bracketed by HIP events on the launch stream.
-    Inter-kernel gaps are included, so this is never below the kernel time."""
-    for _ in range(warm):
-        c.launch()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if use_graph:
-        g = capture(torch, lambda: [c.launch() for _ in range(reps)])
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-    else:
-        e0.record()
-        for _ in range(reps):
-            c.launch()
-        e1.record()
-    e1.synchronize()
-    return e0.elapsed_time(e1) / reps
-
-
 def case_summary(c):
     ms = c.avg_ms
     d = {"ms": round(ms, 6)}
@@ -252,44 +238,125 @@ def traffic_for(case_name):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inputs, gpu_outputs):
-    """The fp64 oracle on the same host bytes as the GPU GEMV cases (all
-    rows; a bounded sample of a few seconds of CPU work), plus a parity check
-    of the GPU outputs against it."""
-    import numpy as np
-
+def cpu_baseline(inputs, gpu_outputs, min_seconds):
+    """The fp64 CPU oracle on the same host bytes as the GPU GEMV calls: all
+    rows of every call, repeated until at least `min_seconds` of wall time
+    (a bounded sample), plus a parity check of the GPU outputs against it."""
     import oracle
 
     orc = oracle.get()
-    tot_bytes, tot_s, worst = 0, 0.0, 0.0
-    done = []
-    for name, (fmt, W, x, N, K) in inputs.items():
-        if fmt not in ("q4_0", "q4_k"):
-            continue
-        t0 = time.perf_counter()
-        ref = orc.gemv_q4_0(W, x, N, K) if fmt == "q4_0" else orc.gemv_q4_k(W, x, N, K)
-        dt = time.perf_counter() - t0
-        b = x.shape[0]
-        tot_bytes += W.nbytes + b * K * 4 + b * N * 4
-        tot_s += dt
-        done.append(name)
-        if name in gpu_outputs:
-            rel, nmax = oracle.errors(gpu_outputs[name], ref)
-            worst = max(worst, rel, nmax)
-    if not done:
+    gemv = [(n, v) for n, v in inputs.items() if v[0] in ("q4_0", "q4_k")]
+    if not gemv:
         return None, None
+    tot_bytes, passes, worst = 0, 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        for name, (fmt, W, x, N, K) in gemv:
+            ref = orc.gemv_q4_0(W, x, N, K) if fmt == "q4_0" else orc.gemv_q4_k(W, x, N, K)
+            b = x.shape[0]
+            tot_bytes += W.nbytes + b * K * 4 + b * N * 4
+            if passes == 0 and name in gpu_outputs:
+                rel, nmax = oracle.errors(gpu_outputs[name], ref)
+                worst = max(worst, rel, nmax)
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    tot_s = time.perf_counter() - t0
+    names = ", ".join(n for n, _ in gemv)
     return ({"value": round(tot_bytes / tot_s / 1e9, 3), "unit": "GB/s", "cores": orc.threads,
              "kind": "oracle",
-             "sample": f"all rows of the step's {len(done)} GEMV calls ({', '.join(done)}), "
-                       f"{tot_s:.1f} s of CPU time, fp64 dequantize-then-multiply"},
+             "sample": f"{passes} passes over all rows of the step's {len(gemv)} GEMV calls "
+                       f"({names}); {tot_s:.1f} s wall on {orc.threads} threads; fp64 "
+                       "dequantize-then-multiply"},
             worst)
+
+
+# ---- rocprofv3 summaries (host only) -------------------------------------------
+
+def _short_kernel(name):
+    import re
+    name = re.sub(r"lqmm::\(anonymous namespace\)::", "", name)
+    name = re.sub(r"\(.*\)$", "", name)
+    return name.replace("void ", "")
+
+
+def summarize_trace(stats_csv, out_md, command, title):
+    """Markdown table of a `rocprofv3 --kernel-trace --stats` kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\n")
+        f.write("Command, run from the repository root on one MI355X after "
+                "`cd /tmp && export TMPDIR=/tmp` (paths relative to the repository):\n\n")
+        f.write(f"```\n{command}\n```\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | share % |\n"
+                "|---|---:|---:|---:|---:|---:|\n")
+        for r in rows:
+            f.write(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | "
+                    f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |\n")
+
+
+def _counter_means(csv_path, counter, pick):
+    """Mean per-dispatch value of `counter` over the dispatches whose kernel
+    name satisfies pick(name)."""
+    import csv
+    import collections
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and pick(r["Kernel_Name"]):
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} dispatches matched in {csv_path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_traffic(fetch_csv, write_csv, calib_mib, commands):
+    """HBM bytes per launch of the roofline kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
+    reads for the calibration kernel (reads and writes calib_mib MiB)."""
+    kern = lambda n: "gemv_kernel<lqmm::(anonymous namespace)::FmtQ4_K, 1" in n
+    calib = lambda n: "neg_kernel" in n
+    f_k, nf = _counter_means(fetch_csv, "FETCH_SIZE", kern)
+    w_k, nw = _counter_means(write_csv, "WRITE_SIZE", kern)
+    f_c, _ = _counter_means(fetch_csv, "FETCH_SIZE", calib)
+    w_c, _ = _counter_means(write_csv, "WRITE_SIZE", calib)
+    expect_kib = calib_mib * 1024.0
+    fs, ws = expect_kib / f_c, expect_kib / w_c
+    src = os.path.join(ROOT, "block_quantized_matmul_amd", "csrc", "gemv.hip")
+    out = {
+        "case": ROOFLINE_CASE,
+        "kernel": "gemv_kernel<FmtQ4_K, 1, ...> (VALU mode, batch 1)",
+        "kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "dispatches": {"fetch": nf, "write": nw},
+        "fetch_kib_per_dispatch": round(f_k, 1),
+        "write_kib_per_dispatch": round(w_k, 1),
+        "calibration": {"kernel": "torch.neg, float32, out of place", "mib_read": calib_mib,
+                        "mib_written": calib_mib, "fetch_kib": round(f_c, 1),
+                        "write_kib": round(w_c, 1), "fetch_scale": round(fs, 4),
+                        "write_scale": round(ws, 4)},
+        "hbm_bytes_per_launch": int(round((f_k * fs + w_k * ws) * 1024)),
+        "commands": commands,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        stats, out_md, command, title = args.summarize_trace
+        summarize_trace(stats, out_md, command, title)
+        return
+    if args.summarize_traffic:
+        fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write = args.summarize_traffic
+        summarize_traffic(fetch_csv, write_csv, int(calib_mib), [cmd_fetch, cmd_write])
+        return
     if args.gpus != 1:
-        print(f"bench.py: runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
-              "single-GPU build (the multi-GPU sharding is a design note only).", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path is implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -309,49 +376,54 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.calib_copy_mib:
+        # Counter calibration: a plain elementwise kernel that reads and
+        # writes a known number of bytes.
         n = args.calib_copy_mib * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(f"[bench] calibration copy of {args.calib_copy_mib} MiB x3 done", file=sys.stderr,
-              flush=True)
+        del src, dst
+        print(f"[bench] calibration kernel over {args.calib_copy_mib} MiB x3 done",
+              file=sys.stderr, flush=True)
 
-    # per-kernel timing (cold HBM through rotation)
-    for c in cases:
-        c.avg_ms = time_case(torch, c, args.reps, warm=min(5, c.nrot), use_graph=not args.eager)
-        print(f"[bench] {c.name}: {case_summary(c)}", file=sys.stderr, flush=True)
-
-    # whole steps
+    # The K timed steps run case-major: every hot-path call is captured K
+    # times back to back in one HIP graph (each launch on the next weight
+    # copy), and the graphs are replayed in step order, each bracketed by HIP
+    # events on the launch stream. This is the same work as K step-major
+    # passes, with the graph-launch overhead spread over K launches; the
+    # events give each call's average launch duration inside the timed region.
     gemv = [c for c in cases if c.kind == "gemv"]
-    others = [c for c in cases if c.kind != "gemv"]
-    order = gemv + others
-    def step():
+    order = gemv + [c for c in cases if c.kind != "gemv"]
+    if args.eager:
+        run = {c.name: (lambda c=c, n=args.steps: [c.launch() for _ in range(n)]) for c in order}
+        warm = {c.name: (lambda c=c, n=args.warmup: [c.launch() for _ in range(n)]) for c in order}
+    else:
+        run, warm = {}, {}
         for c in order:
-            c.launch()
-
-    # Four captured steps, replayed in turn, so that a weight copy is reused
-    # only after four steps (> 1 GB of other traffic).
-    graphs = [] if args.eager else [capture(torch, step) for _ in range(4)]
-
-    def run_step(i):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
-            step()
-
-    for i in range(args.warmup):
-        run_step(i)
+            g = capture(torch, lambda c=c: [c.launch() for _ in range(args.steps)])
+            run[c.name] = g.replay
+            if args.warmup:
+                gw = capture(torch, lambda c=c: [c.launch() for _ in range(args.warmup)])
+                warm[c.name] = gw.replay
+    for c in order:
+        if c.name in warm:
+            warm[c.name]()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        run_step(i)
-    e1.record()
-    e1.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i, c in enumerate(order):
+        run[c.name]()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / max(1, args.steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    for i, c in enumerate(order):
+        c.avg_ms = ev[i].elapsed_time(ev[i + 1]) / args.steps
+        print(f"[bench] {c.name}: {case_summary(c)}", file=sys.stderr, flush=True)
+    ms_per_step = sum(c.avg_ms for c in order)
+    roof = [c for c in gemv if c.name == ROOFLINE_CASE]
 
     gpu_out = {c.name: c.make_out() for c in gemv}
 
@@ -370,34 +442,38 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16*f16->f32 (q4/q8 weights dequantized exactly; fp32 GEMM in f32)",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": "llama_layer_set: Q4_0 GEMV K=4096 N=4096/11008/12288 b1+b4; "
                         "Q4_K GEMV N=28672 K=8192 b1+b8; Q8_0xf16 GEMM 512x14336x4096; "
                         "fp32 GEMM 2048^3",
             "weights": "cold HBM (rotated copies >= 512 MiB per set)",
+            "value_is": "GEMV algorithmic bytes / GEMV share of the timed steps (case-major)",
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4) if value else None,
+            "wall_ms_per_step_host": round(wall_ms / max(1, args.steps), 4),
         },
     }
-    rc = next((c for c in cases if c.name == ROOFLINE_CASE), None)
-    if rc is not None:
+    if roof:
+        rc = roof[0]
         ach = rc.bytes / (rc.avg_ms * 1e-3) / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": traffic_for(ROOFLINE_CASE),
-                            "kernel": "gemv_kernel<FmtQ4_K,1,R> (" + ROOFLINE_CASE + ")",
+                            "kernel": "gemv_kernel<FmtQ4_K, 1, ...> (" + ROOFLINE_CASE + ")",
                             "algorithmic_bytes_per_launch": rc.bytes,
                             "avg_launch_ms": round(rc.avg_ms, 6)}
-    gc = next((c for c in cases if c.kind == "gemm_f16"), None)
-    if gc is not None:
-        tf = gc.flops / (gc.avg_ms * 1e-3) / 1e12
-        line["prefill_gemm"] = {"tflops": round(tf, 1), "peak": F16_PEAK_TFLOPS,
-                                "frac": round(tf / F16_PEAK_TFLOPS, 4), "ms": round(gc.avg_ms, 6)}
-    line["cases"] = {c.name: case_summary(c) for c in cases}
+    for kind, key, peak in (("gemm_f16", "prefill_gemm", F16_PEAK_TFLOPS),
+                            ("gemm_f32", "fp32_gemm", F32_PEAK_TFLOPS)):
+        gc = next((c for c in cases if c.kind == kind), None)
+        if gc is not None:
+            tf = gc.flops / (gc.avg_ms * 1e-3) / 1e12
+            line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
+                         "ms": round(gc.avg_ms, 6)}
+    line["cases"] = {c.name: case_summary(c) for c in order}
 
     if not args.no_cpu_baseline:
-        base, worst = cpu_baseline(inputs, gpu_out)
+        base, worst = cpu_baseline(inputs, gpu_out, args.cpu_seconds)
         line["cpu_baseline"] = base
         if worst is not None:
             line["parity_vs_oracle_max_err"] = float(f"{worst:.3e}")

@@ -97,7 +97,10 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       if (per_unit * units_total > 80 * 1024) waves = 16;
       if (env_waves == 8 || env_waves == 16) waves = env_waves;
     }
-    const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2) ? env_u : 1) : 0;
+    // Two super-blocks per row per chunk up to six activation rows; one for
+    // larger batches, whose staged activations leave less LDS for the
+    // staging buffers.
+    const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2) ? env_u : (B <= 6 ? 2 : 1)) : 0;
     const int64_t red_bytes =
         mfma ? (int64_t)lqmm::gemv_mfma_reduce_bytes(waves) +
                    (lds_stage ? (int64_t)lqmm::gemv_q4k_lds_stage_bytes(lds_u) : 0)
@@ -127,6 +130,9 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         int uu = lds_stage ? lds_u : 2, ks = waves == 16 ? 4 : 1;
         const int ksmax = waves == 16 ? 16 : 8;
         while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
+        // The coalesced Q4_K kernel runs fastest with all eight waves of a
+        // workgroup on one tile (measured on 28672 x 8192, batch 3 to 8).
+        if (lds_stage) ks = 8;
         if (!lds_stage && (env_u == 2 || env_u == 4)) uu = env_u;
         if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
           ks = env_ks;
@@ -140,7 +146,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         pl.ksplit = ks;
         pl.waves = waves;
         pl.lds_stage = lds_stage;
-        pl.depth = env_depth > 0 ? env_depth : (uu == 1 ? 4 : 2);
+        pl.depth = env_depth > 0 ? env_depth : 2;
         const int teams = waves / ks;
         wg_needed = (tiles + teams - 1) / teams;
       } else {
