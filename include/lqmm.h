@@ -56,9 +56,14 @@
  * Accumulation is fp32 everywhere. The quantized GEMVs round the activations
  * x to fp16 (round to nearest even) before the dot products, so |x| must stay
  * below 65504 and x contributes a relative rounding error of at most 2^-11
- * per element; the dequantized weights are exact. The Q8_0 GEMM rounds each
- * dequantized weight d*q to fp16 (one rounding) and the output to fp16.
- * The fp32 GEMM uses fp32 matrix-core products with fp32 accumulation.
+ * per element. For one or two activation rows per pass the dequantized
+ * weights are exact (the block scales are applied in fp32). From three rows
+ * up the GEMVs run on the fp16 matrix cores and round each dequantized
+ * weight to fp16: Q4_0 once (d*(q-8)); Q4_K rounds d*sc and dmin*m to fp16
+ * once per sub-block and then each weight once (one fused multiply-add).
+ * The Q8_0 GEMM rounds each dequantized weight d*q to fp16 (one rounding)
+ * and the output to fp16. The fp32 GEMM uses fp32 matrix-core products with
+ * fp32 accumulation.
  */
 #ifndef LQMM_H
 #define LQMM_H
@@ -96,7 +101,8 @@ lqmm_status lqmm_sgemm(const float *A, const float *B, float *C,
  * Q4_0 GEMV (decode): y[b][n] = sum_k W[n][k] * x[b][k] for b < batch.
  * W: N x (K/32) Q4_0 blocks (N*K/32*18 bytes); x: batch x K fp32;
  * y: batch x N fp32 (overwritten). K % 32 == 0; any batch >= 1 (the batch
- * rows share each weight load; up to 8 rows per pass).
+ * rows share each weight load: up to 2 rows per pass on the vector ALUs, up
+ * to 16 per pass on the matrix cores, which take over from 3 rows).
  * Dequantization happens in registers ("Llamas na Web", "Design de Shader
  * Consciente de Quantizacao", mat-vec case).
  * workspace/workspace_bytes: optional device scratch; pass NULL/0. The
