@@ -84,10 +84,13 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     if (env_mfma == 0 || env_mfma == 1) mfma = env_mfma == 1;
     const int bmax = mfma ? 16 : 2;
     const int B = (int)(left < bmax ? left : bmax);
-    // Units per launch limited by the LDS budget; whole Q4_K super-blocks.
-    // Q4_K in MFMA mode: coalesced loads staged through LDS (8 waves, one
-    // super-block per row per chunk) unless disabled for tuning.
-    const bool lds_stage = mfma && fmt == GemvFormat::Q4_K && env_ldsk != 0;
+    // MFMA mode uses the coalesced kernel (loads staged through LDS, 8
+    // waves) when rows are whole 256-weight super-chunks of 144 bytes and a
+    // 16-row tile spans less than 2 GiB (32-bit load offsets); otherwise, or
+    // when disabled for tuning, the MFMA-layout kernel.
+    const int sc_units = fmt == GemvFormat::Q4_K ? 4 : 8;  // units per super-chunk
+    const bool lds_stage = mfma && env_ldsk != 0 && units_total % sc_units == 0 &&
+                           16 * row_bytes < ((int64_t)1 << 31);
     // Other MFMA launches: 16-wave workgroups when the staged activations
     // leave room for only one workgroup per CU, so that more loads are in
     // flight.
@@ -103,11 +106,14 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2) ? env_u : (B <= 6 ? 2 : 1)) : 0;
     const int64_t red_bytes =
         mfma ? (int64_t)lqmm::gemv_mfma_reduce_bytes(waves) +
-                   (lds_stage ? (int64_t)lqmm::gemv_q4k_lds_stage_bytes(lds_u) : 0)
+                   (lds_stage ? (int64_t)lqmm::gemv_coal_stage_bytes(lds_u) : 0)
              : 0;
     const int64_t lds_cap = lds_stage ? lqmm::kMaxLds : lqmm::kMaxGemvLds;
     int64_t max_units = (lds_cap - red_bytes) / (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, 1);
+    // K-split launches start on whole Q4_K super-blocks, and on whole
+    // super-chunks for the coalesced kernel.
     if (fmt == GemvFormat::Q4_K) max_units &= ~(int64_t)3;
+    if (lds_stage) max_units -= max_units % sc_units;
     for (int64_t u0 = 0; u0 < units_total; u0 += max_units) {
       const int64_t nu64 = units_total - u0 < max_units ? units_total - u0 : max_units;
       const int nu = (int)nu64;
@@ -130,16 +136,16 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         int uu = lds_stage ? lds_u : 2, ks = waves == 16 ? 4 : 1;
         const int ksmax = waves == 16 ? 16 : 8;
         while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
-        // The coalesced Q4_K kernel runs fastest with all eight waves of a
-        // workgroup on one tile (measured on 28672 x 8192, batch 3 to 8).
+        // The coalesced kernel runs fastest with all eight waves of a
+        // workgroup on one tile (measured on Q4_K 28672 x 8192, batch 3 to 8).
         if (lds_stage) ks = 8;
         if (!lds_stage && (env_u == 2 || env_u == 4)) uu = env_u;
         if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
           ks = env_ks;
-        // every slice must hold whole chunks of 4*uu units
+        // every slice must hold a whole chunk of uu super-chunks
         if (lds_stage) {
-          while (ks > 1 && (nu / ks) < 4 * uu) ks /= 2;
-          if (nu < 4 * uu) uu = 1;
+          while (ks > 1 && (nu / ks) < sc_units * uu) ks /= 2;
+          if (nu < sc_units * uu) uu = 1;
         }
         pl.rows_per_lane = 1;
         pl.units_per_lane = uu;
@@ -221,6 +227,7 @@ lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, in
                                int64_t N, int64_t K, void *stream) {
   if (!W || !X || !Y) return LQMM_ERR_NULL;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || K % 32 != 0) return LQMM_ERR_SHAPE;
+  if (K >= LQMM_GEMM_MAX_K) return LQMM_ERR_SHAPE;  // 32-bit offsets within a 128-row tile
   if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LQMM_ERR_ALIGN;
   int num_cus = 0;
   lqmm_status st = current_device(&num_cus);

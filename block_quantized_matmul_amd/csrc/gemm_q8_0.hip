@@ -5,10 +5,11 @@
 // "Design de Shader Consciente de Quantizacao": quantized blocks are loaded,
 // dequantized into shared memory and reused by the whole M tile. Here the
 // shared memory is the CU's LDS and the reuse feeds
-// v_mfma_f32_16x16x32_f16:
-// * 128x128 output tile per 256-thread workgroup (four waves of 64x64, 4x4
-//   MFMA tiles each); K advances 64 (two Q8_0 blocks) per step through two
-//   LDS buffers, the next step's global loads in flight during the MFMAs;
+// v_mfma_f32_32x32x16_f16:
+// * 128x128 output tile per 256-thread workgroup (four waves of 64x64, 2x2
+//   tiles of v_mfma_f32_32x32x16_f16 each); K advances 64 (two Q8_0 blocks)
+//   per step through two LDS buffers, the global loads of the step after
+//   next in flight during the MFMAs;
 // * each thread fetches one raw 34-byte block (fp16 d + 32 int8) and
 //   dequantizes it in registers: q ^ 0x80 placed in the mantissa of 1024.0
 //   with v_perm_b32 gives the exact fp16 value 1152 + q, one packed subtract
@@ -33,7 +34,10 @@ struct RawQ8 {
 };
 
 __device__ __forceinline__ void dequant_q8_0(const RawQ8 &r, u32x4 (&out)[4]) {
-  const half2_t d2 = as_half2((r.d & 0xFFFF) * 0x10001u);
+  // d arrives zero-extended; taking its low half needs no instruction, and
+  // the packed multiplies broadcast it with op_sel.
+  const half_t dh = __builtin_bit_cast(half_t, (uint16_t)r.d);
+  const half2_t d2 = {dh, dh};
   const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
   uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
 #pragma unroll
@@ -47,6 +51,13 @@ __device__ __forceinline__ void dequant_q8_0(const RawQ8 &r, u32x4 (&out)[4]) {
     out[i >> 1][(i & 1) * 2 + 1] = as_u32(hi);
   }
 }
+
+// Raw global data of one K step for one thread: four 16-byte pieces of the X
+// tile and one Q8_0 block of the W tile.
+struct RawStep {
+  u32x4 x[4];
+  RawQ8 w;
+};
 
 __global__ void __launch_bounds__(kThreads)
 gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
@@ -68,97 +79,133 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t nb = K / 32;
-  const int64_t row_bytes = nb * 34;
+  const uint32_t Ku = (uint32_t)K;
+  const uint32_t row_bytes = Ku / 32 * 34;
+  const int nk = (int)((K + BK - 1) / BK);
+  const bool ragged = K % BK != 0;  // the last step holds one block, not two
 
-  u32x4 rx[4];
-  RawQ8 rw;
-  auto load_tile = [&](int64_t k0) {
+  // The tile's X rows and W rows through buffer resources that end at the
+  // last row of the tensor: loads of rows past M or N return zeros (their
+  // results are never stored). Offsets are 32-bit (the host keeps
+  // BM * K * 2 < 2^32). Nothing is computed from loaded data before it is
+  // written to LDS, so the loads of two steps stay in flight together.
+  const int64_t xrows = M - m0 < BM ? M - m0 : BM;
+  const int64_t wrows = N - n0 < BN ? N - n0 : BN;
+  const rsrc_t xr = make_rsrc(X + m0 * K, (uint32_t)(xrows * K * 2));
+  const rsrc_t wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)(wrows * row_bytes));
+  uint32_t xoff[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + kThreads * it;
+    xoff[it] = ((uint32_t)(idx >> 3) * Ku + 8 * (idx & 7)) * 2;
+  }
+  const int wblk = tid & 1;
+  const uint32_t woff = (uint32_t)(tid >> 1) * row_bytes + 34 * wblk;
+
+  auto load_step = [&](RawStep &r, int kt) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) r.x[it] = buf_load_b128(xr, xoff[it] + kt * (BK * 2));
+    const uint32_t wo = woff + kt * 68;
+    r.w.d = buf_load_u16(wr, wo);
+    r.w.q0 = buf_load_b128(wr, wo + 2);
+    r.w.q1 = buf_load_b128(wr, wo + 18);
+  };
+  auto store_step = [&](int buf, RawStep &r, int kt) {
+    // Keep the scheduler from hoisting work on the loaded values into the
+    // MFMA section, where it would wait for loads still in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    if (ragged && kt == nk - 1) {
+      // Only the first block of this step lies inside K: zero the X pieces
+      // and the W block past it (they were read from the next row).
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        if (8 * ((tid + kThreads * it) & 7) >= 32) r.x[it] = u32x4{0, 0, 0, 0};
+      if (wblk) r.w.d = 0;
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      int idx = tid + kThreads * it;
-      int row = idx >> 3, c = idx & 7;
-      int64_t gm = m0 + row, gk = k0 + 8 * c;
-      rx[it] = (gm < M && gk < K) ? *reinterpret_cast<const u32x4 *>(X + gm * K + gk)
-                                  : u32x4{0, 0, 0, 0};
+      const int idx = tid + kThreads * it;
+      *reinterpret_cast<u32x4 *>(&Xs[buf][(idx >> 3) * LDS_STRIDE + 8 * (idx & 7)]) = r.x[it];
     }
-    {
-      int row = tid >> 1, blk = tid & 1;
-      int64_t gn = n0 + row, kb = k0 / 32 + blk;
-      if (gn < N && kb < nb) {
-        const uint8_t *p = W + gn * row_bytes + kb * 34;
-        rw.d = load_u16(p);
-        rw.q0 = load_u32x4_unaligned(p + 2);
-        rw.q1 = load_u32x4_unaligned(p + 18);
-      } else {
-        rw.d = 0;
-        rw.q0 = u32x4{0, 0, 0, 0};
-        rw.q1 = rw.q0;
-      }
-    }
+    u32x4 out[4];
+    dequant_q8_0(r.w, out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4 *>(&Ws[buf][(tid >> 1) * LDS_STRIDE + 32 * wblk + 8 * j]) = out[j];
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto store_tile = [&](int buf) {
+
+  // Each wave owns a 64 x 64 block as 2 x 2 tiles of v_mfma_f32_32x32x16_f16:
+  // lane l supplies row (or column) l % 32 and the 8 k values 8 * (l / 32)
+  // .. +7 of each operand, and holds D[8 * (v / 4) + 4 * (l / 32) + v % 4]
+  // [l % 32] for v = 0..15.
+  const int l32 = lane & 31, lh = lane >> 5;
+  float16_t acc[2][2];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int idx = tid + kThreads * it;
-      int row = idx >> 3, c = idx & 7;
-      *reinterpret_cast<u32x4 *>(&Xs[buf][row * LDS_STRIDE + 8 * c]) = rx[it];
-    }
-    {
-      int row = tid >> 1, blk = tid & 1;
-      u32x4 out[4];
-      dequant_q8_0(rw, out);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4 *>(&Ws[buf][row * LDS_STRIDE + 32 * blk + 8 * j]) = out[j];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      half8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const half8_t *>(
+            &Xs[buf][(wm * 64 + i * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * lh]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const half8_t *>(
+            &Ws[buf][(wn * 64 + j * 32 + l32) * LDS_STRIDE + kk * 16 + 8 * lh]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   };
 
-  float4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0, 0, 0, 0};
-
-  const int64_t nk = (K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
+  // Software pipeline: the global loads of step kt + 2 are issued before the
+  // MFMAs of step kt, and step kt + 1 (loaded one step earlier) is written
+  // to the other LDS buffer after them, so every load has two steps of
+  // matrix work to arrive. Steps past the end are loaded from clamped
+  // addresses and never used.
+  RawStep ra, rb;
+  load_step(ra, 0);
+  load_step(rb, nk > 1 ? 1 : 0);
+  store_step(0, ra, 0);
   __syncthreads();
-
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      half8_t a[4], b[4];
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-        a[ti] = *reinterpret_cast<const half8_t *>(
-            &Xs[cur][(wm * 64 + ti * 16 + li) * LDS_STRIDE + kk * 32 + 8 * lg]);
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj)
-        b[tj] = *reinterpret_cast<const half8_t *>(
-            &Ws[cur][(wn * 64 + tj * 16 + li) * LDS_STRIDE + kk * 32 + 8 * lg]);
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj)
-          acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ti], b[tj], acc[ti][tj], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    load_step(ra, kt + 2);
+    compute(0);
+    store_step(1, rb, kt + 1);
     __syncthreads();
+    load_step(rb, kt + 3 < nk ? kt + 3 : kt + 2);
+    compute(1);
+    store_step(0, ra, kt + 2);
+    __syncthreads();
+  }
+  compute(0);
+  if (kt + 1 < nk) {
+    store_step(1, rb, kt + 1);
+    __syncthreads();
+    compute(1);
   }
 
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      const int64_t col = n0 + wn * 64 + tj * 16 + li;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + l32;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = m0 + wm * 64 + ti * 16 + 4 * lg + v;
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (row < M && col < N)
-          Y[row * N + col] = __builtin_bit_cast(uint16_t, (half_t)acc[ti][tj][v]);
+          Y[row * N + col] = __builtin_bit_cast(uint16_t, (half_t)acc[i][j][v]);
       }
     }
 }
@@ -170,7 +217,7 @@ hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, in
   (void)num_cus;
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if (tiles > 0x7fffffff || (int64_t)BM * K * 2 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_q8_0_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, W, X, Y,
                      M, N, K, (int)tiles_n);
   return hipGetLastError();

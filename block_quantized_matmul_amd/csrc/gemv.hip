@@ -34,6 +34,8 @@
 // with the staged activations (row = batch row) as the A operand. The matrix
 // core does the k reduction, so the per-weight VALU cost no longer grows with
 // the batch.
+#include <type_traits>
+
 #include "lqmm_device.hpp"
 #include "lqmm_internal.hpp"
 
@@ -366,20 +368,49 @@ struct FmtQ4_K {
 // ---- activation staging ------------------------------------------------------
 // Word (b, u, t) holds the 8 activations of word t of unit u for batch row b,
 // in unpack order; `hi_scale` multiplies the hi values (1/16 in VALU mode so
-// that (1024 + 16q) * x/16 = 64x + qx, 1 in MFMA mode). `index(b, u, t)` gives
-// the word's LDS slot; consecutive threads write consecutive slots.
+// that (1024 + 16q) * x/16 = 64x + qx, 1 in MFMA mode).
+struct XWord {
+  float4_t lo, hi;
+};
 template <class F>
-__device__ __forceinline__ u32x4 stage_word(const float *__restrict__ x, int64_t ldx, int b,
-                                            int u, int t, float hi_scale) {
+__device__ __forceinline__ XWord load_xword(const float *__restrict__ x, int64_t ldx, int b, int u,
+                                            int t) {
   const float *base = x + b * ldx + (int64_t)u * F::kUnitWeights + 4 * t;
-  float4_t lo = *reinterpret_cast<const float4_t *>(base);
-  float4_t hi = *reinterpret_cast<const float4_t *>(base + F::kUnitWeights / 2) * hi_scale;
+  return XWord{*reinterpret_cast<const float4_t *>(base),
+               *reinterpret_cast<const float4_t *>(base + F::kUnitWeights / 2)};
+}
+__device__ __forceinline__ u32x4 pack_xword(const XWord &w, float hi_scale) {
+  const float4_t hi = w.hi * hi_scale;
   u32x4 word;
-  word.x = pack_half2(lo.x, lo.z);
+  word.x = pack_half2(w.lo.x, w.lo.z);
   word.y = pack_half2(hi.x, hi.z);
-  word.z = pack_half2(lo.y, lo.w);
+  word.z = pack_half2(w.lo.y, w.lo.w);
   word.w = pack_half2(hi.y, hi.w);
   return word;
+}
+
+// Stage words 0 .. total-1 into xs; `coords(i, b, u, t)` names word i. Each
+// thread keeps kBatch words' loads in flight (clamped indices, so the loads
+// are unconditional and the compiler waits once per batch, not once per
+// word).
+template <class F, int kThreads, int kBatch, class Coords>
+__device__ __forceinline__ void stage_words(u32x4 *xs, int total, const float *__restrict__ x,
+                                            int64_t ldx, float hi_scale, Coords coords) {
+  for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
+    XWord w[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = base + k * kThreads;
+      int b, u, t;
+      coords(i < total ? i : total - 1, b, u, t);
+      w[k] = load_xword<F>(x, ldx, b, u, t);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = base + k * kThreads;
+      if (i < total) xs[i] = pack_xword(w[k], hi_scale);
+    }
+  }
 }
 
 // Sum of the lo (x, z halves) and hi (y, w halves) values of a staged word.
@@ -444,10 +475,12 @@ gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int
   load(buf0, g < ngroups ? g : ngroups - 1, 0);
 
   // Stage: slot (b*T + t)*nu + u, u fastest; then the per-(b, u) sums.
-  for (int i = tid; i < B * T * nu; i += kGemvThreads) {
-    const int u = i % nu, bt = i / nu;
-    xs[i] = stage_word<F>(x, ldx, bt / T, u, bt % T, 0.0625f);
-  }
+  // (one or two words per thread at batch 1 and 2: no batching)
+  stage_words<F, kGemvThreads, 1>(xs, B * T * nu, x, ldx, 0.0625f, [&](int i, int &b, int &u, int &t) {
+    u = i % nu;
+    b = i / nu / T;
+    t = i / nu % T;
+  });
   __syncthreads();
   for (int i = tid; i < B * nu; i += kGemvThreads) {
     const int u = i % nu, b = i / nu;
@@ -592,10 +625,11 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   int c = 0;
   load(buf0, gb + team, 0);
 
-  for (int i = tid; i < nb * T * nu; i += kThreads) {
-    const int b = i % nb, tu = i / nb;
-    xs[i] = stage_word<F>(x, ldx, b, tu % nu, tu / nu, 1.0f);
-  }
+  stage_words<F, kThreads, 4>(xs, nb * T * nu, x, ldx, 1.0f, [&](int i, int &b, int &u, int &t) {
+    b = i % nb;
+    u = i / nb % nu;
+    t = i / nb / nu;
+  });
   __syncthreads();
 
   const UnpackMasks kmask;
@@ -682,123 +716,190 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   }
 }
 
-// ---- Q4_K MFMA mode with coalesced loads --------------------------------------
-// Same decomposition as gemv_mfma_kernel (tiles of 16 rows, KS k-slices per
-// team), but a chunk is U whole super-blocks of each of the 16 rows, and it
-// is fetched with coalesced loads: piece p (16 bytes) of the chunk goes to
-// lane p % 64 of load p / 64, so consecutive lanes read consecutive bytes of
-// a row. The pieces are written to a wave-private LDS buffer and read back in
-// the MFMA B-operand layout (lane l: row l % 16, units (l/16)*U .. +U-1).
-// The MFMA-layout loads of gemv_mfma_kernel touch 16 rows per instruction and
-// keep the L1 address path stalled; these touch one to four rows.
-// D chunks are kept in flight per wave through a ring of D register buffers
-// (chunk i is consumed from buffer i % D, which then receives chunk i + D).
-template <int U, int KS, int D>
-__global__ void __launch_bounds__(kGemvThreads)
-gemv_q4k_lds_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
-                    const float *__restrict__ x, int64_t ldx, float *__restrict__ y,
-                    int64_t ldy, int64_t N, int nb, int accumulate) {
+// ---- MFMA mode with coalesced loads (Q4_K and Q4_0) ---------------------------
+// Both formats pack 256 weights of a row into 144 bytes: one Q4_K super-block
+// or eight Q4_0 blocks (a "super-chunk", 16-byte aligned in every row whose
+// byte length is a multiple of 16). A chunk is U super-chunks of each of the
+// 16 rows of a tile. It is fetched with coalesced 16-byte buffer loads
+// (piece p of the chunk goes to lane p % 64 of load p / 64, so consecutive
+// lanes read consecutive bytes of a row), written to a wave-private LDS
+// buffer and read back in the MFMA B-operand layout: lane l takes row l % 16
+// and 64 weights of each super-chunk (lane group q = l / 16 takes Q4_K
+// sub-block pair q, or Q4_0 blocks 2q and 2q + 1). The MFMA-layout loads of
+// gemv_mfma_kernel touch 16 rows per instruction and keep the address unit
+// stalled; these touch one to four rows.
+//
+// Load addresses: every lane's byte offset within the 16-row tile is fixed
+// (row * row_bytes + piece * 16, in a VGPR); the tile base goes in the
+// buffer resource and the chunk offset in the scalar offset. The resource
+// ends at the last row of the matrix, so rows past N read zeros; unused
+// piece slots get an offset past the resource and read zeros too.
+// D chunks are in flight per wave through a ring of D register buffers.
+
+// Q4_K: unit = sub-block pair (64 weights); 4 units per super-chunk, one per
+// lane group.
+struct CoalQ4_K {
   using F = FmtQ4_K;
+  static constexpr int kUnitsPerSC = 4;
+  static constexpr int kLaneUnits = 1;
+  // Unit j of lane group q in the super-chunk at `sc` (16-byte pieces).
+  static __device__ __forceinline__ F::Raw read(const u32x4 *sc, int q, int /*j*/) {
+    F::Raw r;
+    r.h = sc[0];
+    r.q0 = sc[1 + 2 * q];
+    r.q1 = sc[2 + 2 * q];
+    return r;
+  }
+};
+
+// Q4_0: unit = one block (32 weights, 18 bytes at byte 18 * b of the
+// super-chunk); 8 units per super-chunk, blocks 2q and 2q + 1 for lane group
+// q. Their 36 bytes start 4-byte aligned; the even block's codes start 2
+// bytes into a dword and are realigned with v_alignbyte_b32.
+struct CoalQ4_0 {
+  using F = FmtQ4_0;
+  static constexpr int kUnitsPerSC = 8;
+  static constexpr int kLaneUnits = 2;
+  static __device__ __forceinline__ F::Raw read(const u32x4 *sc, int q, int j) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(sc) + 9 * q;
+    F::Raw r;
+    if (j == 0) {
+      const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3], d4 = w[4];
+      r.d = d0 & 0xFFFFu;
+      r.q = u32x4{__builtin_amdgcn_alignbyte(d1, d0, 2), __builtin_amdgcn_alignbyte(d2, d1, 2),
+                  __builtin_amdgcn_alignbyte(d3, d2, 2), __builtin_amdgcn_alignbyte(d4, d3, 2)};
+    } else {
+      r.d = w[4] >> 16;
+      r.q = u32x4{w[5], w[6], w[7], w[8]};
+    }
+    return r;
+  }
+};
+
+template <class C, int U, int KS, int D>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
+                 const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int64_t ldy,
+                 int64_t N, int nb, int accumulate) {
+  using F = typename C::F;
   constexpr int NW = kWavesPerWg;
   constexpr int T = F::kWords;
   constexpr int kTeams = NW / KS;
-  constexpr int PR = 9 * U;             // 16-byte pieces per row per chunk
-  constexpr int NP = 16 * PR;           // pieces per chunk
-  constexpr int NI = (NP + 63) / 64;    // loads per lane per chunk
+  constexpr int PR = 9 * U;           // 16-byte pieces per row per chunk
+  constexpr int NP = 16 * PR;         // pieces per chunk
+  constexpr int NI = (NP + 63) / 64;  // loads per lane per chunk
+  constexpr int UPC = U * C::kUnitsPerSC;  // units per chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (t*nu + u)*nb + b
   float4_t *red = reinterpret_cast<float4_t *>(smem + (size_t)nb * T * nu * 16);
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int team = wave / KS, slice = wave % KS;
   const int lane = tid & (kWave - 1);
   const int n = lane & 15;
   const int q = lane >> 4;
   u32x4 *wbuf = reinterpret_cast<u32x4 *>(smem + (size_t)nb * T * nu * 16 + NW * kWave * 16) +
                 wave * NI * kWave;
-  const int64_t ngroups = (N + 15) / 16;
-  const int units_per_chunk = 4 * U;
-  const int nus = (((nu + KS - 1) / KS) + units_per_chunk - 1) / units_per_chunk * units_per_chunk;
+  const int ngroups = (int)((N + 15) / 16);
+  // Units per slice, a whole number of chunks; every slice runs the same
+  // number of chunks (units past the end of its range are zeroed).
+  const int nus = (((nu + KS - 1) / KS) + UPC - 1) / UPC * UPC;
   const int ubeg = slice * nus;
   const int uend = ubeg + nus < nu ? ubeg + nus : nu;
-  const int nchunks = nus / units_per_chunk;
-  const int64_t group_stride = (int64_t)gridDim.x * kTeams;
+  const int nchunks = nus / UPC;
+  const int group_stride = gridDim.x * kTeams;
+  const uint32_t unit0_bytes = (uint32_t)(unit0 / C::kUnitsPerSC * 144);
 
-  // First unit of chunk c, moved back so the chunk ends inside the row
-  // (nu is a multiple of 4U here).
+  // First unit of chunk c, moved back so that the chunk ends inside the row
+  // (nu is a multiple of kUnitsPerSC, so the start stays on a super-chunk).
   auto chunk_start = [&](int c) -> int {
-    const int u = ubeg + c * units_per_chunk;
-    return u + units_per_chunk <= nu ? u : nu - units_per_chunk;
+    const int u = ubeg + c * UPC;
+    return u + UPC <= nu ? u : nu - UPC;
   };
 
-  // Chunk c of group gg (clamped to the last group) into dst.
-  auto load = [&](u32x4 (&dst)[NI], int64_t gg, int c) {
-    const int64_t gc = gg < ngroups ? gg : ngroups - 1;
-    const int64_t sb0 = (unit0 + chunk_start(c)) >> 2;
+  uint32_t off[NI];
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      int pc = k * kWave + lane;
-      pc = pc < NP ? pc : NP - 1;
-      int64_t row = gc * 16 + pc / PR;
-      row = row < N ? row : N - 1;
-      dst[k] = *reinterpret_cast<const u32x4 *>(W + row * row_bytes + sb0 * 144 + (pc % PR) * 16);
+  for (int k = 0; k < NI; ++k) {
+    const int pc = k * kWave + lane;
+    off[k] = pc < NP ? (uint32_t)(pc / PR) * (uint32_t)row_bytes + (uint32_t)(pc % PR) * 16
+                     : 0x80000000u;
+  }
+
+  // Chunk c of tile g (clamped to the last tile) into dst.
+  auto load = [&](u32x4 (&dst)[NI], int g, int c) {
+    const int gc = g < ngroups ? g : ngroups - 1;
+    const int64_t r0 = (int64_t)gc * 16;
+    const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+    const rsrc_t rs = make_rsrc(W + r0 * row_bytes + unit0_bytes,
+                                (uint32_t)(rows * row_bytes - unit0_bytes));
+    const int soff = chunk_start(c) / C::kUnitsPerSC * 144;
+#pragma unroll
+    for (int k = 0; k < NI; ++k)
+      dst[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off[k], soff, 0));
+  };
+
+  // Items of this wave: chunk c of tile g, c running fastest; g starts at
+  // blockIdx.x * kTeams + team and steps by group_stride. Every wave of the
+  // workgroup runs the same number of items (the workgroup loops while its
+  // first team's tile is in range), so the barriers of the reduction match.
+  u32x4 bufs[D][NI];
+  int pg = blockIdx.x * kTeams, pc = 0;  // next item to prefetch (tile of team 0)
+  auto advance = [&](int &g, int &c) {
+    if (++c == nchunks) {
+      c = 0;
+      g += group_stride;
     }
   };
-
-  u32x4 bufs[D][NI];
-  const int64_t gbase = (int64_t)blockIdx.x * kTeams;  // first group of this workgroup
-  // Item i of this wave: chunk i % nchunks of group gbase + (i / nchunks) *
-  // group_stride + team. The workgroup loops while that group index (without
-  // the team) is below ngroups, so all its waves run the same iterations.
-  auto item_gb = [&](int64_t i) { return gbase + (i / nchunks) * group_stride; };
-  auto load_item = [&](u32x4 (&dst)[NI], int64_t i) {
-    load(dst, item_gb(i) + team, (int)(i % nchunks));
-  };
 #pragma unroll
-  for (int k = 0; k < D; ++k) load_item(bufs[k], k);
-
-  for (int i = tid; i < nb * T * nu; i += kGemvThreads) {
-    const int b = i % nb, tu = i / nb;
-    xs[i] = stage_word<F>(x, ldx, b, tu % nu, tu / nu, 1.0f);
+  for (int k = 0; k < D; ++k) {
+    load(bufs[k], pg + team, pc);
+    advance(pg, pc);
   }
+
+  stage_words<F, kGemvThreads, 4>(xs, nb * T * nu, x, ldx, 1.0f, [&](int i, int &b, int &u, int &t) {
+    b = i % nb;
+    u = i / nb % nu;
+    t = i / nb / nu;
+  });
   __syncthreads();
 
   const UnpackMasks kmask;
   float4_t acc = float4_t{0, 0, 0, 0};
-  const int xb = n < nb ? n : 0;
+  const int xb = n < nb ? n : 0;  // rows >= nb are computed but never stored
+  int cg = blockIdx.x * kTeams, cc = 0;  // item being consumed
 
-  // Consume buffer `src` (item i), then refill it with item i + D.
-  auto stage = [&](u32x4 (&src)[NI], int64_t i) {
-    const int c = (int)(i % nchunks);
-    const int64_t gb = item_gb(i);
+  // Consume buffer `src` (item (cg, cc)), then refill it with the item D
+  // places later.
+  auto stage = [&](u32x4 (&src)[NI]) {
     // Wave-private transpose through LDS; one wave's LDS operations complete
     // in order, so the reads below see these writes.
 #pragma unroll
     for (int k = 0; k < NI; ++k) wbuf[k * kWave + lane] = src[k];
-    load_item(src, i + D);
-    const int nominal = ubeg + c * units_per_chunk;
-    const int ustart = chunk_start(c);
+    load(src, pg + team, pc);
+    advance(pg, pc);
+    const int nominal = ubeg + cc * UPC;
+    const int ustart = chunk_start(cc);
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int ul = q * U + j;               // unit within the chunk
-      const int u = ustart + ul;
-      const bool valid = u >= nominal && u < uend;
-      const u32x4 *pb = wbuf + n * PR + (ul >> 2) * 9;
-      F::Raw r;
-      r.h = pb[0];
-      r.q0 = pb[1 + 2 * (ul & 3)];
-      r.q1 = pb[2 + 2 * (ul & 3)];
-      const F::Prep pr = F::prep(r, ul & 3, valid);
-      const u32x4 *xrow = xs + (int64_t)u * nb + xb;
+    for (int s = 0; s < U; ++s) {
+      const u32x4 *sc = wbuf + n * PR + 9 * s;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const half8_t a = __builtin_bit_cast(half8_t, xrow[t * nu * nb]);
-        const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(r, pr, t, kmask));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wv, acc, 0, 0, 0);
+      for (int j = 0; j < C::kLaneUnits; ++j) {
+        const int ul = s * C::kUnitsPerSC + q * C::kLaneUnits + j;  // unit within the chunk
+        const int u = ustart + ul;
+        const bool valid = u >= nominal && u < uend;
+        const typename F::Raw r = C::read(sc, q, j);
+        const typename F::Prep pr = F::prep(r, q, valid);
+        const u32x4 *xrow = xs + u * nb + xb;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const half8_t a = __builtin_bit_cast(half8_t, xrow[t * nu * nb]);
+          const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(r, pr, t, kmask));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wv, acc, 0, 0, 0);
+        }
       }
     }
-    if (c == nchunks - 1) {
+    if (cc == nchunks - 1) {
       if (KS > 1) {
         red[wave * kWave + lane] = acc;
         __syncthreads();
@@ -807,9 +908,9 @@ gemv_q4k_lds_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t un
           for (int s2 = 1; s2 < KS; ++s2) acc += red[(wave + s2) * kWave + lane];
         }
       }
-      const int64_t g = gb + team;
+      const int g = cg + team;
       if (slice == 0 && g < ngroups) {
-        const int64_t row = g * 16 + n;
+        const int64_t row = (int64_t)g * 16 + n;
         if (row < N) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -825,15 +926,14 @@ gemv_q4k_lds_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t un
       acc = float4_t{0, 0, 0, 0};
       if (KS > 1) __syncthreads();
     }
+    advance(cg, cc);
   };
 
-  int64_t i = 0;
-  while (item_gb(i) < ngroups) {
+  while (cg < ngroups) {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      stage(bufs[k], i);
-      ++i;
-      if (item_gb(i) >= ngroups) break;
+      stage(bufs[k]);
+      if (cg >= ngroups) break;
     }
   }
 }
@@ -860,14 +960,14 @@ hipError_t launch_valu(const GemvPlan &pl, const uint8_t *W, const float *x, flo
   return hipGetLastError();
 }
 
-template <int U, int KS, int D>
-hipError_t launch_q4k_lds(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
-                          hipStream_t stream) {
-  auto kern = gemv_q4k_lds_kernel<U, KS, D>;
+template <class C, int U, int KS, int D>
+hipError_t launch_coal(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                       hipStream_t stream) {
+  auto kern = gemv_coal_kernel<C, U, KS, D>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
@@ -875,6 +975,27 @@ hipError_t launch_q4k_lds(const GemvPlan &pl, const uint8_t *W, const float *x, 
                      pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
                      pl.accumulate);
   return hipGetLastError();
+}
+
+// Coalesced-kernel instances: U in {1, 2}, KS in {1, 2, 4, 8}, depth 2 (3 for
+// tuning sweeps).
+template <class C>
+hipError_t launch_coal_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                           hipStream_t s) {
+#define LQMM_COAL(UU, DD)                                                    \
+  switch (pl.ksplit) {                                                       \
+    case 1: return launch_coal<C, UU, 1, DD>(pl, W, x, y, s);                \
+    case 2: return launch_coal<C, UU, 2, DD>(pl, W, x, y, s);                \
+    case 4: return launch_coal<C, UU, 4, DD>(pl, W, x, y, s);                \
+    default: return launch_coal<C, UU, 8, DD>(pl, W, x, y, s);               \
+  }
+  if (pl.units_per_lane == 2) {
+    if (pl.depth >= 3) { LQMM_COAL(2, 3) }
+    LQMM_COAL(2, 2)
+  }
+  if (pl.depth >= 3) { LQMM_COAL(1, 3) }
+  LQMM_COAL(1, 2)
+#undef LQMM_COAL
 }
 
 template <class F, int R, int U, int KS, int NW>
@@ -910,21 +1031,8 @@ hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, floa
   if (pl.mfma) {
     const int u = pl.units_per_lane;
     if (pl.lds_stage) {
-#define LQMM_Q4K_LDS(UU, DD)                                                  \
-  switch (pl.ksplit) {                                                       \
-    case 1: return launch_q4k_lds<UU, 1, DD>(pl, W, x, y, s);                \
-    case 2: return launch_q4k_lds<UU, 2, DD>(pl, W, x, y, s);                \
-    case 4: return launch_q4k_lds<UU, 4, DD>(pl, W, x, y, s);                \
-    default: return launch_q4k_lds<UU, 8, DD>(pl, W, x, y, s);               \
-  }
-      if (u == 2) {
-        if (pl.depth >= 3) { LQMM_Q4K_LDS(2, 3) }
-        LQMM_Q4K_LDS(2, 2)
-      }
-      if (pl.depth >= 6) { LQMM_Q4K_LDS(1, 6) }
-      if (pl.depth >= 4) { LQMM_Q4K_LDS(1, 4) }
-      LQMM_Q4K_LDS(1, 2)
-#undef LQMM_Q4K_LDS
+      if (std::is_same<F, FmtQ4_K>::value) return launch_coal_fmt<CoalQ4_K>(pl, W, x, y, s);
+      return launch_coal_fmt<CoalQ4_0>(pl, W, x, y, s);
     }
     if (pl.waves == 16) {
       switch (pl.ksplit) {
@@ -963,7 +1071,7 @@ size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu) {
 
 size_t gemv_mfma_reduce_bytes(int waves) { return (size_t)waves * kWave * 16; }
 
-size_t gemv_q4k_lds_stage_bytes(int u) {
+size_t gemv_coal_stage_bytes(int u) {
   return (size_t)kWavesPerWg * ((16 * 9 * u + 63) / 64) * kWave * 16;
 }
 

@@ -49,6 +49,22 @@ __device__ __forceinline__ uint32_t load_u16(const uint8_t *p) {
   return v;
 }
 
+// ---- buffer loads -----------------------------------------------------------
+// A raw buffer resource covers [base, base + nbytes); a load whose offset
+// (the VGPR offset plus the immediate; the SGPR offset is not checked) lies
+// past nbytes returns zeros without touching memory. Word 3 selects 32-bit
+// untyped access on gfx9-family GPUs.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_u16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 // ---- cross-lane sums with DPP -------------------------------------------
 // dpp<CTRL, ROW_MASK>(v): v read from the lane selected by CTRL; rows that
 // ROW_MASK disables read 0.

@@ -21,8 +21,9 @@ struct GemvPlan {
   int units_per_lane; // units each lane loads per chunk: VALU (R, U) in {(1,2),(1,4),(2,1),(2,2)}
   int ksplit;         // MFMA mode: waves sharing one tile along K (1..8; 4..16 with 16 waves)
   int waves;          // MFMA mode: waves per workgroup (8 or 16)
-  int lds_stage;      // MFMA mode, Q4_K: coalesced loads staged through LDS (8 waves)
-  int depth;          // lds_stage: chunks in flight per wave (2, 4 or 6 with U = 1; 2 or 3 with U = 2)
+  int lds_stage;      // MFMA mode: coalesced loads staged through LDS (8 waves; units_per_lane = U
+                      // super-chunks of 256 weights per row per chunk)
+  int depth;          // lds_stage: chunks in flight per wave (2 or 3)
   int lpr_log2;       // log2(lanes sharing one weight row)
   int nu;             // units (of gemv_unit_weights weights) per row in this launch
   int64_t unit0;      // first unit of each row covered by this launch
@@ -36,7 +37,7 @@ struct GemvPlan {
 
 size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu);
 size_t gemv_mfma_reduce_bytes(int waves);  // extra LDS of an MFMA-mode launch
-size_t gemv_q4k_lds_stage_bytes(int u);     // per-workgroup staging of the coalesced Q4_K kernel
+size_t gemv_coal_stage_bytes(int u);        // per-workgroup staging of the coalesced MFMA kernel
 constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 int gemv_unit_weights(GemvFormat f);
 int gemv_threads();

@@ -87,6 +87,8 @@ typedef enum {
 
 /* Largest size accepted for any dimension (elements). */
 #define LQMM_MAX_DIM ((int64_t)1 << 31)
+/* lqmm_gemm_q8_0_f16 needs K < LQMM_GEMM_MAX_K (LQMM_ERR_SHAPE otherwise). */
+#define LQMM_GEMM_MAX_K ((int64_t)1 << 24)
 
 /*
  * Dense fp32 GEMM: C[M x N] = A[M x K] * B[K x N], all fp32 row-major.
@@ -115,7 +117,8 @@ lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y,
 /*
  * Q8_0 x fp16 GEMM (prefill): Y[m][n] = sum_k X[m][k] * W[n][k], i.e.
  * Y = X * W^T. W: N x (K/32) Q8_0 blocks; X: M x K fp16; Y: M x N fp16
- * (fp32 accumulation, rounded to nearest even at the end). K % 32 == 0.
+ * (fp32 accumulation, rounded to nearest even at the end). K % 32 == 0 and
+ * K < LQMM_GEMM_MAX_K.
  * Weight blocks are dequantized to fp16 into LDS and reused by every row
  * of the M tile ("Llamas na Web", "Design de Shader Consciente de
  * Quantizacao", matmul case).

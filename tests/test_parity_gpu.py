@@ -40,7 +40,12 @@ def _run_q4_k(c):
 Q4_0_SMALL = [(1, 32, 1), (7, 32, 3), (5, 64, 2), (13, 96, 1), (33, 288, 5), (64, 1024, 8),
               (100, 4096, 4), (1, 4096, 9), (3, 9216, 8), (257, 2048, 16), (2, 160, 7),
               (1000, 512, 1), (31, 8192, 2), (17, 1024, 17), (40, 18432, 18), (129, 4096, 3),
-              (16, 512, 16), (3, 36864, 3)]
+              (16, 512, 16), (3, 36864, 3),
+              # matrix-core path through the coalesced kernel (K a multiple of
+              # 256): one super-chunk, ragged tiles, several slices and K-split
+              # launches
+              (257, 256, 5), (33, 768, 16), (300, 2048, 3), (17, 512, 40), (1, 256, 3),
+              (3, 36864, 4), (4096, 4096, 4)]
 
 
 @pytest.mark.parametrize("N,K,B", Q4_0_SMALL)
