@@ -227,7 +227,7 @@ lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, in
                                int64_t N, int64_t K, void *stream) {
   if (!W || !X || !Y) return LQMM_ERR_NULL;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || K % 32 != 0) return LQMM_ERR_SHAPE;
-  if (K >= LQMM_GEMM_MAX_K) return LQMM_ERR_SHAPE;  // 32-bit offsets within a 128-row tile
+  if (K >= LQMM_GEMM_MAX_K) return LQMM_ERR_SHAPE;  // 31-bit load offsets within a tile
   if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LQMM_ERR_ALIGN;
   int num_cus = 0;
   lqmm_status st = current_device(&num_cus);

@@ -2,27 +2,234 @@
 // accumulation, fp16 output, on the gfx950 fp16 matrix cores.
 //
 // This is the matmul case of "Resumo Tecnico: Llamas na Web", section
-// "Design de Shader Consciente de Quantizacao": quantized blocks are loaded,
-// dequantized into shared memory and reused by the whole M tile. Here the
-// shared memory is the CU's LDS and the reuse feeds
-// v_mfma_f32_32x32x16_f16:
-// * 128x128 output tile per 256-thread workgroup (four waves of 64x64, 2x2
-//   tiles of v_mfma_f32_32x32x16_f16 each); K advances 64 (two Q8_0 blocks)
-//   per step through two LDS buffers, the global loads of the step after
-//   next in flight during the MFMAs;
-// * each thread fetches one raw 34-byte block (fp16 d + 32 int8) and
-//   dequantizes it in registers: q ^ 0x80 placed in the mantissa of 1024.0
-//   with v_perm_b32 gives the exact fp16 value 1152 + q, one packed subtract
-//   gives q, one packed multiply gives fp16(d*q) (a single rounding); the 32
-//   fp16 weights go to LDS as four 16-byte stores;
-// * both operands sit k-contiguous in LDS, so each MFMA operand is one
-//   ds_read_b128; X rows and W rows use the same k order, which is all the
-//   dot product needs.
+// "Design de Shader Consciente de Quantizacao": quantized blocks are loaded
+// into shared memory (the CU's LDS), dequantized and reused by every row of
+// the M tile.
+//
+// * One 256-thread workgroup per 128 x 256 output tile; wave w owns columns
+//   64w .. 64w+63 of the tile and all 128 rows, as 4 x 2 tiles of
+//   v_mfma_f32_32x32x16_f16.
+// * (K % 64 == 0; otherwise the register-staged kernel at the end of this
+//   file runs.) K advances 64 (two Q8_0 blocks) per step through a ring of NS LDS
+//   stages. Each stage holds the X tile (128 rows x 64 fp16) and the raw W
+//   tile (256 rows x 68 bytes: both blocks of every row, as stored), both
+//   written by buffer-to-LDS loads issued NS - 1 steps ahead. Raw Q8_0 bytes
+//   in LDS cost about half the LDS write bandwidth of dequantized fp16, and
+//   LDS writes run at about half the rate of LDS reads on this GPU.
+// * Each wave dequantizes its own columns once per step, from LDS straight
+//   into MFMA B operands (so each weight is dequantized once per workgroup
+//   and reused by all 128 rows): q ^ 0x80 placed in the mantissa of 1024.0
+//   with v_perm_b32 is exactly 1152 + q; a packed subtract gives q and a
+//   packed multiply gives fp16(d*q), one rounding.
+// * K order inside a step: MFMA slice s (16 k) takes, in lane half h, the
+//   codes 8s .. 8s+7 of block h. A operands (X) are read in the same order;
+//   the X tile is stored with 16-byte chunks permuted per row pair so that
+//   those reads are free of LDS bank conflicts.
 #include "lqmm_device.hpp"
 #include "lqmm_internal.hpp"
 
 namespace lqmm {
 namespace {
+
+constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int NS = 4;                            // LDS stages
+constexpr int kXStageBytes = BM * BK * 2;        // 16 KB
+constexpr int kWRowDwords = BK / 32 * 34 / 4;    // 17 dwords of raw W per row per step
+constexpr int kWStageBytes = BN * kWRowDwords * 4;  // 17 KB
+constexpr int kStageBytes = kXStageBytes + kWStageBytes;
+constexpr int kXLoads = kXStageBytes / 16 / kThreads;         // 16-byte loads per thread per step
+constexpr int kWLoads = kWStageBytes / 4 / kThreads;          // 4-byte loads per thread per step
+constexpr int kLoadsPerStep = kXLoads + kWLoads;               // per wave, counted by vmcnt
+static_assert(kXStageBytes % (16 * kThreads) == 0 && kWStageBytes % (4 * kThreads) == 0, "");
+static_assert(NS >= 2 && (NS - 2) * kLoadsPerStep <= 63, "vmcnt range");
+
+// Slot of 16-byte chunk c (0..7) of X tile row r: chunks permuted per row
+// pair, so that the 16 rows one ds_read_b128 phase touches hit 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int xslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Wait until at most N of this wave's buffer loads are outstanding and all
+// its LDS reads are done, then join the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// fp16 weights d*q of 4 int8 codes (one dword) as two fp16 pairs.
+__device__ __forceinline__ void dequant_word(uint32_t w, half2_t d2, uint32_t &lo, uint32_t &hi) {
+  const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
+  const uint32_t u = w ^ 0x80808080u;
+  half2_t l = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
+  half2_t h = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+  lo = as_u32((l - bias) * d2);
+  hi = as_u32((h - bias) * d2);
+}
+
+__global__ void __launch_bounds__(kThreads)
+gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
+                 uint16_t *__restrict__ Y, int64_t M, int64_t N, int64_t K, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+  // L2. Renumber so that consecutive logical tiles (the M tiles that share
+  // one weight N tile) run on the same XCD and share its L2.
+  // (32-bit scalar arithmetic: the host keeps the tile count below 2^31, and
+  // the buffer resources built from these values must stay in scalar
+  // registers.)
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int ntiles = tiles_m * tiles_n;
+  int tile = blockIdx.x;
+  if (ntiles % 8 == 0) tile = (tile % 8) * (ntiles / 8) + tile / 8;
+  tile = __builtin_amdgcn_readfirstlane(tile);
+  const int64_t m0 = (int64_t)(tile % tiles_m) * BM, n0 = (int64_t)(tile / tiles_m) * BN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const uint32_t Ku = (uint32_t)K;
+  const uint32_t row_bytes = Ku / 32 * 34;
+  const int nk = (int)(K / BK);  // K % 64 == 0 here
+
+  // Buffer resources over the tile's rows, ending at the last row of each
+  // tensor: rows past M or N read zeros (their results are never stored).
+  // Offsets are 32-bit (the host keeps BN * row_bytes and BM * K * 2 below
+  // 2^31).
+  const int64_t xrows = M - m0 < BM ? M - m0 : BM;
+  const int64_t wrows = N - n0 < BN ? N - n0 : BN;
+  const rsrc_t xr = make_rsrc(X + m0 * K, (uint32_t)(xrows * K * 2));
+  const rsrc_t wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)(wrows * row_bytes));
+
+  // Per-lane source offsets of this wave's buffer-to-LDS loads. Load i of
+  // wave w fills 64 consecutive LDS slots of the stage (16 bytes each for X,
+  // 4 bytes each for W); lane L fills slot L. The lane's offset within the
+  // tile is fixed (a VGPR); the step's offset goes in the scalar offset.
+  // Every byte a step reads lies inside its own row (K % 64 == 0), and rows
+  // past M or N start past the end of the resource, so they read zeros.
+  uint32_t xoff[kXLoads], woff[kWLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int slot = (wave * kXLoads + i) * 64 + lane;  // 16-byte slot of the X stage
+    const int r = slot >> 3, c = xslot(r, slot & 7);     // slot & 7 holds chunk c of row r
+    xoff[i] = (uint32_t)r * Ku * 2 + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < kWLoads; ++i) {
+    const int dw = (wave * kWLoads + i) * 64 + lane;  // dword of the W stage
+    woff[i] = (uint32_t)(dw / kWRowDwords) * row_bytes + 4 * (dw % kWRowDwords);
+  }
+  // Loads of step kt into stage buffer kt % NS. Steps past the end load the
+  // last step again (never read), so that every step counts the same in
+  // vmcnt.
+  auto issue = [&](int kt) {
+    uint8_t *st = smem + (kt % NS) * kStageBytes;
+    const int ks = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (wave * kXLoads + i) * 1024, 16,
+                                               (int)xoff[i], ks * (BK * 2), 0, 0);
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, st + kXStageBytes + (wave * kWLoads + i) * 256,
+                                               4, (int)woff[i], ks * 68, 0, 0);
+  };
+
+  float16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+
+  // B operands of one step from the raw W tile of stage `st`: this lane's
+  // column (two groups of 32) and block h; slice s uses codes 8s .. 8s+7.
+  auto dequant_step = [&](const uint8_t *st, half8_t (&b)[2][4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t *rw = reinterpret_cast<const uint32_t *>(st + kXStageBytes) +
+                           (wave * 64 + j * 32 + l32) * kWRowDwords;
+      // block h: d at byte 34h, codes at byte 34h + 2 (dword 9h, offset 2 - 2h).
+      // Block 0 needs dwords 0..8 of the row; block 1 dwords 9..16 (its
+      // ninth read, unused at offset 0, takes dword 16 to stay in the row).
+      const uint32_t dword = rw[8 * h];
+      uint32_t q[9];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = rw[9 * h + i];
+      q[8] = rw[8 + 8 * h];
+      const uint32_t dbits = __builtin_amdgcn_ubfe(dword, 16 * h, 16);
+      const half_t dh = __builtin_bit_cast(half_t, (uint16_t)dbits);
+      const half2_t d2 = {dh, dh};
+      const uint32_t shift = 2 - 2 * h;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t w0 = __builtin_amdgcn_alignbyte(q[2 * s + 1], q[2 * s], shift);
+        uint32_t w1 = __builtin_amdgcn_alignbyte(q[2 * s + 2], q[2 * s + 1], shift);
+        uint32_t p0, p1, p2, p3;
+        dequant_word(w0, d2, p0, p1);
+        dequant_word(w1, d2, p2, p3);
+        b[j][s] = __builtin_bit_cast(half8_t, u32x4{p0, p1, p2, p3});
+      }
+    }
+  };
+  // The MFMAs of one step: A operands from the X tile of stage `st`, slice
+  // by slice.
+  auto mfma_step = [&](const uint8_t *st, const half8_t (&b)[2][4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8_t a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + l32;
+        a[i] = *reinterpret_cast<const half8_t *>(st + r * 128 + 16 * xslot(r, 4 * h + s));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j][s], acc[i][j], 0, 0, 0);
+    }
+  };
+  for (int kt = 0; kt < nk; ++kt) {
+    // Step kt's loads (this wave's, then everyone's) have landed, and every
+    // wave is done reading the buffer the next issue overwrites.
+    wait_and_barrier<(NS - 2) * kLoadsPerStep>();
+    issue(kt + NS - 1);
+    const uint8_t *st = smem + (kt % NS) * kStageBytes;
+    half8_t b[2][4];
+    dequant_step(st, b);
+    mfma_step(st, b);
+  }
+  // Drain the loads issued past the end before the workgroup exits.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // D layout of v_mfma_f32_32x32x16_f16: lane l holds column l % 32 and rows
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4 for v = 0..15.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wave * 64 + j * 32 + l32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < M && col < N)
+          Y[row * N + col] = __builtin_bit_cast(uint16_t, (half_t)acc[i][j][v]);
+      }
+    }
+}
+
+// ---- any K % 32 == 0 ----------------------------------------------------------
+// When K % 64 == 32, rows of W are not a whole number of dwords per 64-k step
+// and the last step holds a single block; this kernel loads each thread's
+// 34-byte block with exact-size global loads into registers instead. It is
+// the same method with a 128 x 128 tile: the blocks of a step are loaded,
+// dequantized to fp16 into LDS (two buffers) and reused by the whole M tile;
+// the global loads of step kt + 2 are in flight during the MFMAs of step kt.
+namespace k32 {
 
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;  // halves per LDS row (144 bytes)
@@ -60,7 +267,7 @@ struct RawStep {
 };
 
 __global__ void __launch_bounds__(kThreads)
-gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
+gemm_q8_0_k32_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
                  uint16_t *__restrict__ Y, int64_t M, int64_t N, int64_t K, int tiles_n) {
   __shared__ __attribute__((aligned(16))) half_t Xs[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) half_t Ws[2][BN * LDS_STRIDE];
@@ -210,16 +417,38 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
     }
 }
 
+}  // namespace k32
+
 }  // namespace
 
 hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,
                             int64_t N, int64_t K, int num_cus, hipStream_t stream) {
   (void)num_cus;
+  if (K % 64 != 0) {
+    const int64_t tiles_m = (M + k32::BM - 1) / k32::BM, tiles_n = (N + k32::BN - 1) / k32::BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffff || (int64_t)k32::BM * K * 2 >= ((int64_t)1 << 32))
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k32::gemm_q8_0_k32_kernel, dim3((unsigned)tiles), dim3(k32::kThreads), 0,
+                       stream, W, X, Y, M, N, K, (int)tiles_n);
+    return hipGetLastError();
+  }
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
-  if (tiles > 0x7fffffff || (int64_t)BM * K * 2 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_q8_0_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, W, X, Y,
-                     M, N, K, (int)tiles_n);
+  // Load offsets (and the out-of-range marker 2^31) must fit in 31 bits.
+  if (tiles > 0x7fffffff || (int64_t)BM * K * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)BN * (K / 32 * 34) >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_q8_0_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       NS * kStageBytes);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(gemm_q8_0_kernel, dim3((unsigned)tiles), dim3(kThreads), NS * kStageBytes,
+                     stream, W, X, Y, M, N, K, (int)tiles_n);
   return hipGetLastError();
 }
 

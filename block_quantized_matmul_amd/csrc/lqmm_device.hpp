@@ -54,9 +54,17 @@ __device__ __forceinline__ uint32_t load_u16(const uint8_t *p) {
 // (the VGPR offset plus the immediate; the SGPR offset is not checked) lies
 // past nbytes returns zeros without touching memory. Word 3 selects 32-bit
 // untyped access on gfx9-family GPUs.
+// base and nbytes must be the same in every lane; they are read from the
+// first active lane, so that the resource lives in scalar registers (a
+// resource the compiler cannot prove uniform makes it loop over lanes).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)nbytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(hi << 32 | lo), 0,
+                                           __builtin_amdgcn_readfirstlane((int)nbytes),
+                                           0x00020000);
 }
 __device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));

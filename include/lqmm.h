@@ -88,7 +88,7 @@ typedef enum {
 /* Largest size accepted for any dimension (elements). */
 #define LQMM_MAX_DIM ((int64_t)1 << 31)
 /* lqmm_gemm_q8_0_f16 needs K < LQMM_GEMM_MAX_K (LQMM_ERR_SHAPE otherwise). */
-#define LQMM_GEMM_MAX_K ((int64_t)1 << 24)
+#define LQMM_GEMM_MAX_K ((int64_t)1 << 22)
 
 /*
  * Dense fp32 GEMM: C[M x N] = A[M x K] * B[K x N], all fp32 row-major.

@@ -93,7 +93,7 @@ def test_gemm_argument_errors(lib):
     assert f(A16, A16, A16, 0, 4, 32, None) == ERR_SHAPE
     assert f(A16, A16, A16, 4, 0, 32, None) == ERR_SHAPE
     assert f(A16, A16, A16, 4, 4, 48, None) == ERR_SHAPE
-    assert f(A16, A16, A16, 4, 4, 1 << 24, None) == ERR_SHAPE  # K limit of the GEMM
+    assert f(A16, A16, A16, 4, 4, 1 << 22, None) == ERR_SHAPE  # K limit of the GEMM
     assert f(A16, A8, A16, 4, 4, 32, None) == ERR_ALIGN
 
 

@@ -210,7 +210,10 @@ def test_q4_k_extreme_codes(orc):
 
 # ------------------------------------------------------------- Q8_0 GEMM
 Q8_0_SMALL = [(1, 1, 32), (3, 5, 64), (17, 130, 96), (128, 128, 64), (130, 257, 320),
-              (64, 200, 4096), (256, 512, 1024), (1, 300, 32)]
+              (64, 200, 4096), (256, 512, 1024), (1, 300, 32),
+              # ragged in every dimension at once: partial 128 x 256 tiles and a
+              # last K step holding a single block
+              (129, 257, 160), (300, 513, 224), (512, 768, 4128)]
 
 
 @pytest.mark.parametrize("M,N,K", Q8_0_SMALL)
