@@ -33,24 +33,32 @@ namespace {
 
 constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int NS = 4;                            // LDS stages
-constexpr int kXStageBytes = BM * BK * 2;        // 16 KB
-constexpr int kWRowDwords = BK / 32 * 34 / 4;    // 17 dwords of raw W per row per step
-constexpr int kWStageBytes = BN * kWRowDwords * 4;  // 17 KB
-constexpr int kStageBytes = kXStageBytes + kWStageBytes;
-constexpr int kXLoads = kXStageBytes / 16 / kThreads;         // 16-byte loads per thread per step
-constexpr int kWLoads = kWStageBytes / 4 / kThreads;          // 4-byte loads per thread per step
-constexpr int kLoadsPerStep = kXLoads + kWLoads;               // per wave, counted by vmcnt
-static_assert(kXStageBytes % (16 * kThreads) == 0 && kWStageBytes % (4 * kThreads) == 0, "");
-static_assert(NS >= 2 && (NS - 2) * kLoadsPerStep <= 63, "vmcnt range");
+constexpr int NS = 4;                        // LDS stages of the X tile
+constexpr int kXStageBytes = BM * BK * 2;    // 16 KB
+constexpr int kXLoads = kXStageBytes / 16 / kThreads;  // 16-byte loads per thread per step
+// Raw W: each wave owns 64 rows of the tile. A step is 68 bytes of a row,
+// fetched as five 16-byte pieces at byte 0, 16, 32, 48 and 52 (the last two
+// overlap, so nothing past the row's step is read) and kept in the wave's
+// own LDS area as an 80-byte record per row, two steps deep.
+constexpr int kWRows = 64;                   // rows per wave
+constexpr int kWRec = 80;                    // LDS bytes per row record
+constexpr int kWPieces = 5;
+constexpr int kWLoads = kWRows * kWPieces / 64;  // 16-byte loads per lane per step
+constexpr int kWWaveBytes = 2 * kWRows * kWRec;  // per wave, two steps
+constexpr int kLdsBytes = NS * kXStageBytes + 4 * kWWaveBytes;
+// Loads a wave issues per step (W to registers, X to LDS), as vmcnt counts
+// them.
+constexpr int kLoadsPerStep = kXLoads + kWLoads;
+static_assert(kXStageBytes % (16 * kThreads) == 0 && kWRows * kWPieces % 64 == 0, "");
+static_assert(NS >= 3 && (NS - 2) * kLoadsPerStep <= 63, "vmcnt range");
 
 // Slot of 16-byte chunk c (0..7) of X tile row r: chunks permuted per row
 // pair, so that the 16 rows one ds_read_b128 phase touches hit 16 distinct
 // 16-byte bank groups.
 __device__ __forceinline__ int xslot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Wait until at most N of this wave's buffer loads are outstanding and all
-// its LDS reads are done, then join the workgroup barrier.
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// and all its LDS operations are done, then join the workgroup barrier.
 template <int N>
 __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -74,10 +82,9 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
   const int tid = threadIdx.x;
   // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
   // L2. Renumber so that consecutive logical tiles (the M tiles that share
-  // one weight N tile) run on the same XCD and share its L2.
-  // (32-bit scalar arithmetic: the host keeps the tile count below 2^31, and
-  // the buffer resources built from these values must stay in scalar
-  // registers.)
+  // one weight N tile) run on the same XCD and share its L2. (32-bit scalar
+  // arithmetic: the host keeps the tile count below 2^31, and the buffer
+  // resources built from these values must stay in scalar registers.)
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int ntiles = tiles_m * tiles_n;
   int tile = blockIdx.x;
@@ -93,47 +100,96 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
 
   // Buffer resources over the tile's rows, ending at the last row of each
   // tensor: rows past M or N read zeros (their results are never stored).
-  // Offsets are 32-bit (the host keeps BN * row_bytes and BM * K * 2 below
-  // 2^31).
   const int64_t xrows = M - m0 < BM ? M - m0 : BM;
   const int64_t wrows = N - n0 < BN ? N - n0 : BN;
   const rsrc_t xr = make_rsrc(X + m0 * K, (uint32_t)(xrows * K * 2));
   const rsrc_t wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)(wrows * row_bytes));
 
-  // Per-lane source offsets of this wave's buffer-to-LDS loads. Load i of
-  // wave w fills 64 consecutive LDS slots of the stage (16 bytes each for X,
-  // 4 bytes each for W); lane L fills slot L. The lane's offset within the
-  // tile is fixed (a VGPR); the step's offset goes in the scalar offset.
-  // Every byte a step reads lies inside its own row (K % 64 == 0), and rows
-  // past M or N start past the end of the resource, so they read zeros.
-  uint32_t xoff[kXLoads], woff[kWLoads];
+  // Per-lane source offsets within the tile (VGPRs); the step's offset goes
+  // in the scalar offset. Every byte a step reads lies inside its own row
+  // (K % 64 == 0), and rows past M or N start past the end of the resource.
+  // X: buffer-to-LDS load i of wave w fills 64 consecutive 16-byte slots of
+  // the stage; lane L fills slot L.
+  uint32_t xoff[kXLoads];
 #pragma unroll
   for (int i = 0; i < kXLoads; ++i) {
-    const int slot = (wave * kXLoads + i) * 64 + lane;  // 16-byte slot of the X stage
-    const int r = slot >> 3, c = xslot(r, slot & 7);     // slot & 7 holds chunk c of row r
+    const int slot = (wave * kXLoads + i) * 64 + lane;
+    const int r = slot >> 3, c = xslot(r, slot & 7);  // slot & 7 holds chunk c of row r
     xoff[i] = (uint32_t)r * Ku * 2 + 16 * c;
   }
+  // W: piece p = 64 i + lane of this wave's 320 pieces: row p / 5, piece
+  // p % 5; it goes to byte 16 p of the wave's record area (80 bytes a row).
+  uint32_t woff[kWLoads];
 #pragma unroll
   for (int i = 0; i < kWLoads; ++i) {
-    const int dw = (wave * kWLoads + i) * 64 + lane;  // dword of the W stage
-    woff[i] = (uint32_t)(dw / kWRowDwords) * row_bytes + 4 * (dw % kWRowDwords);
+    const int p = 64 * i + lane, rr = p / kWPieces, k = p % kWPieces;
+    woff[i] = (uint32_t)(wave * kWRows + rr) * row_bytes + (k < 4 ? 16 * k : 52);
   }
-  // Loads of step kt into stage buffer kt % NS. Steps past the end load the
-  // last step again (never read), so that every step counts the same in
-  // vmcnt.
-  auto issue = [&](int kt) {
-    uint8_t *st = smem + (kt % NS) * kStageBytes;
-    const int ks = kt < nk ? kt : nk - 1;
+  uint8_t *const wl = smem + NS * kXStageBytes + wave * kWWaveBytes;  // this wave's W records
+
+  auto issue_x = [&](int kt) {
+    const int ks = kt < nk ? kt : nk - 1;  // past the end: reload the last step, never read
+    uint8_t *st = smem + (kt % NS) * kXStageBytes;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (wave * kXLoads + i) * 1024, 16,
                                                (int)xoff[i], ks * (BK * 2), 0, 0);
+  };
+  auto load_w = [&](u32x4 (&rw)[kWLoads], int kt) {
+    const int ks = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, st + kXStageBytes + (wave * kWLoads + i) * 256,
-                                               4, (int)woff[i], ks * 68, 0, 0);
+      rw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)woff[i],
+                                                                              ks * 68, 0));
+  };
+  auto store_w = [&](const u32x4 (&rw)[kWLoads], int buf) {
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i)
+      *reinterpret_cast<u32x4 *>(wl + buf * (kWRows * kWRec) + 16 * (64 * i + lane)) = rw[i];
   };
 
+  // B operands of one step from this wave's W records: column group j
+  // (rows 32 j + l % 32 of the wave) and block h; slice s uses codes
+  // 8s .. 8s+7. Record layout: bytes 0..63 of the step at 0..63, bytes
+  // 52..67 at 64..79, so byte b >= 64 sits at b + 12. Block 0: d and codes
+  // in dwords 0..8 (codes 2 bytes in); block 1: d in the high half of
+  // dword 8, codes in dwords 9..15 and 19 (aligned).
+  // Raw reads of one step's records (column group j = 0, 1), and the
+  // dequantization of slice s from them.
+  struct Raw {
+    uint32_t q[2][9];
+    uint32_t d[2];
+  };
+  auto raw_read = [&](int buf, Raw &r) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t *rw =
+          reinterpret_cast<const uint32_t *>(wl + buf * (kWRows * kWRec) + (32 * j + l32) * kWRec);
+      r.d[j] = rw[8 * h];
+#pragma unroll
+      for (int i = 0; i < 7; ++i) r.q[j][i] = rw[9 * h + i];
+      r.q[j][7] = rw[7 + 12 * h];
+      r.q[j][8] = rw[8 + 11 * h];  // unused for block 1 (offset 0)
+    }
+  };
+  auto dequant_slice = [&](const Raw &r, int s, half8_t (&b)[2][4]) {
+    const uint32_t shift = 2 - 2 * h;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const half_t dh = __builtin_bit_cast(half_t, (uint16_t)__builtin_amdgcn_ubfe(r.d[j], 16 * h, 16));
+      const half2_t d2 = {dh, dh};
+      const uint32_t w0 = __builtin_amdgcn_alignbyte(r.q[j][2 * s + 1], r.q[j][2 * s], shift);
+      const uint32_t w1 = __builtin_amdgcn_alignbyte(r.q[j][2 * s + 2], r.q[j][2 * s + 1], shift);
+      uint32_t p0, p1, p2, p3;
+      dequant_word(w0, d2, p0, p1);
+      dequant_word(w1, d2, p2, p3);
+      b[j][s] = __builtin_bit_cast(half8_t, u32x4{p0, p1, p2, p3});
+    }
+  };
+
+  // Each wave owns a 128 x 64 block of the tile as 4 x 2 tiles of
+  // v_mfma_f32_32x32x16_f16: lane l supplies row (or column) l % 32 and the
+  // 8 k values 8 * (l / 32) .. +7 of each operand.
   float16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -142,67 +198,77 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s);
-
-  // B operands of one step from the raw W tile of stage `st`: this lane's
-  // column (two groups of 32) and block h; slice s uses codes 8s .. 8s+7.
-  auto dequant_step = [&](const uint8_t *st, half8_t (&b)[2][4]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t *rw = reinterpret_cast<const uint32_t *>(st + kXStageBytes) +
-                           (wave * 64 + j * 32 + l32) * kWRowDwords;
-      // block h: d at byte 34h, codes at byte 34h + 2 (dword 9h, offset 2 - 2h).
-      // Block 0 needs dwords 0..8 of the row; block 1 dwords 9..16 (its
-      // ninth read, unused at offset 0, takes dword 16 to stay in the row).
-      const uint32_t dword = rw[8 * h];
-      uint32_t q[9];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = rw[9 * h + i];
-      q[8] = rw[8 + 8 * h];
-      const uint32_t dbits = __builtin_amdgcn_ubfe(dword, 16 * h, 16);
-      const half_t dh = __builtin_bit_cast(half_t, (uint16_t)dbits);
-      const half2_t d2 = {dh, dh};
-      const uint32_t shift = 2 - 2 * h;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint32_t w0 = __builtin_amdgcn_alignbyte(q[2 * s + 1], q[2 * s], shift);
-        uint32_t w1 = __builtin_amdgcn_alignbyte(q[2 * s + 2], q[2 * s + 1], shift);
-        uint32_t p0, p1, p2, p3;
-        dequant_word(w0, d2, p0, p1);
-        dequant_word(w1, d2, p2, p3);
-        b[j][s] = __builtin_bit_cast(half8_t, u32x4{p0, p1, p2, p3});
-      }
-    }
-  };
-  // The MFMAs of one step: A operands from the X tile of stage `st`, slice
-  // by slice.
-  auto mfma_step = [&](const uint8_t *st, const half8_t (&b)[2][4]) {
+  u32x4 rw[kWLoads];  // W step kt + 1 during iteration kt, then step kt + 2
+  // Iteration kt: write W step kt + 1 (in registers) to record buffer
+  // (kt + 1) & 1, request W step kt + 2 into the same registers and X step
+  // kt + NS - 1; then the MFMAs of step kt (B operands `cur`, dequantized in
+  // the previous iteration) with step kt + 1's dequantization (into `next`)
+  // interleaved, slice by slice, so that matrix-core and vector-ALU work
+  // overlap within the wave. When step kt's X stage is read, the loads
+  // issued after it are W and X of the NS - 2 previous iterations; the
+  // prologue waits for all of its own loads.
+  auto iteration = [&](int kt, const half8_t (&cur)[2][4], half8_t (&next)[2][4]) {
+    wait_and_barrier<(NS - 2) * kLoadsPerStep>();
+    store_w(rw, (kt + 1) & 1);
+    load_w(rw, kt + 2);
+    issue_x(kt + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    Raw r;
+    raw_read((kt + 1) & 1, r);
+    const uint8_t *st = smem + (kt % NS) * kXStageBytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8_t a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 32 * i + l32;
-        a[i] = *reinterpret_cast<const half8_t *>(st + r * 128 + 16 * xslot(r, 4 * h + s));
+        const int row = 32 * i + l32;
+        a[i] = *reinterpret_cast<const half8_t *>(st + row * 128 + 16 * xslot(row, 4 * h + s));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j][s], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], cur[j][s], acc[i][j], 0, 0, 0);
+      dequant_slice(r, s, next);
+    }
+    // Scheduling hint: the raw reads and the first A reads, then per slice
+    // eight MFMAs each followed by a few VALU instructions, with the next
+    // slice's A reads in between.
+    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (m == 3 && s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
     }
   };
-  for (int kt = 0; kt < nk; ++kt) {
-    // Step kt's loads (this wave's, then everyone's) have landed, and every
-    // wave is done reading the buffer the next issue overwrites.
-    wait_and_barrier<(NS - 2) * kLoadsPerStep>();
-    issue(kt + NS - 1);
-    const uint8_t *st = smem + (kt % NS) * kStageBytes;
-    half8_t b[2][4];
-    dequant_step(st, b);
-    mfma_step(st, b);
+
+  // Pipeline. X: buffer-to-LDS loads NS - 1 steps ahead, shared by the
+  // workgroup (one barrier per step). W: each wave's own rows, loaded into
+  // registers two steps ahead and written to the wave's record buffer one
+  // step ahead (only this wave reads it, and one wave's LDS operations
+  // complete in order, so no barrier is needed).
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue_x(s);
+  load_w(rw, 0);
+  store_w(rw, 0);
+  load_w(rw, 1);
+  half8_t b0[2][4], b1[2][4];
+  {
+    Raw r;
+    raw_read(0, r);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dequant_slice(r, s, b0);
   }
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    iteration(kt, b0, b1);
+    iteration(kt + 1, b1, b0);
+  }
+  if (kt < nk) iteration(kt, b0, b1);
   // Drain the loads issued past the end before the workgroup exits.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -285,7 +351,6 @@ gemm_q8_0_k32_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int li = lane & 15, lg = lane >> 4;
   const uint32_t Ku = (uint32_t)K;
   const uint32_t row_bytes = Ku / 32 * 34;
   const int nk = (int)((K + BK - 1) / BK);
@@ -443,11 +508,11 @@ hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, in
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_q8_0_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       NS * kStageBytes);
+                                       kLdsBytes);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(gemm_q8_0_kernel, dim3((unsigned)tiles), dim3(kThreads), NS * kStageBytes,
+  hipLaunchKernelGGL(gemm_q8_0_kernel, dim3((unsigned)tiles), dim3(kThreads), kLdsBytes,
                      stream, W, X, Y, M, N, K, (int)tiles_n);
   return hipGetLastError();
 }

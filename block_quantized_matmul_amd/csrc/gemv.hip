@@ -88,9 +88,6 @@ __device__ __forceinline__ half2_t h2(float v) { return half2_t{(half_t)v, (half
 __device__ __forceinline__ half2_t pk_fma(half2_t a, half2_t b, half2_t c) {
   return __builtin_elementwise_fma(a, b, c);
 }
-__device__ __forceinline__ half8_t cat(half2_t a, half2_t b, half2_t c, half2_t d) {
-  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
 
 // ---- Q4_0: unit = one block of 32 weights ----------------------------------
 // Word t (t = 0..3) of the block's qs holds lo positions 4t..4t+3 and hi
