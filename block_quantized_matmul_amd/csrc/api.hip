@@ -100,10 +100,12 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       if (per_unit * units_total > 80 * 1024) waves = 16;
       if (env_waves == 8 || env_waves == 16) waves = env_waves;
     }
-    // Two super-blocks per row per chunk up to six activation rows; one for
-    // larger batches, whose staged activations leave less LDS for the
-    // staging buffers.
-    const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2) ? env_u : (B <= 6 ? 2 : 1)) : 0;
+    // One super-chunk per row per chunk, two for large N at up to six
+    // activation rows (long K-slices; the staged activations leave room).
+    const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2)
+                                       ? env_u
+                                       : (B <= 6 && N > 6 * 16 * (int64_t)num_cus ? 2 : 1))
+                                : 0;
     const int64_t red_bytes =
         mfma ? (int64_t)lqmm::gemv_mfma_reduce_bytes(waves) +
                    (lds_stage ? (int64_t)lqmm::gemv_coal_stage_bytes(lds_u) : 0)
@@ -125,7 +127,9 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       pl.lpr_log2 = lpr_log2;
       pl.lds_bytes = lqmm::gemv_lds_bytes(fmt, mfma, B, nu) + red_bytes;
       int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
-      const int64_t wg_cap = env_wgcu > 0 ? env_wgcu : 2;
+      // The coalesced kernel runs one workgroup per CU: each workgroup stages
+      // all of x, so more workgroups mostly add staging traffic.
+      const int64_t wg_cap = env_wgcu > 0 ? env_wgcu : (lds_stage ? 1 : 2);
       if (wg_per_cu > wg_cap) wg_per_cu = wg_cap;
       if (wg_per_cu < 1) wg_per_cu = 1;
       int64_t wg_needed;
@@ -136,9 +140,10 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         int uu = lds_stage ? lds_u : 2, ks = waves == 16 ? 4 : 1;
         const int ksmax = waves == 16 ? 16 : 8;
         while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
-        // The coalesced kernel runs fastest with all eight waves of a
-        // workgroup on one tile (measured on Q4_K 28672 x 8192, batch 3 to 8).
-        if (lds_stage) ks = 8;
+        // Coalesced kernel: all eight waves on one tile (eight K-slices) up
+        // to three tiles per CU; fewer, longer slices for larger N (measured
+        // on N = 4096 .. 28672, K = 4096 and 8192, batch 3 to 8).
+        if (lds_stage) ks = tiles <= 3 * (int64_t)num_cus ? 8 : tiles <= 6 * (int64_t)num_cus ? 2 : 1;
         if (!lds_stage && (env_u == 2 || env_u == 4)) uu = env_u;
         if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
           ks = env_ks;
