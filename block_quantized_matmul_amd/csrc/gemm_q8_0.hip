@@ -6,9 +6,10 @@
 // into shared memory (the CU's LDS), dequantized and reused by every row of
 // the M tile.
 //
-// * One 256-thread workgroup per 128 x 256 output tile; wave w owns columns
-//   64w .. 64w+63 of the tile and all 128 rows, as 4 x 2 tiles of
-//   v_mfma_f32_32x32x16_f16.
+// * One 512-thread workgroup per 128 x 256 output tile; wave w owns columns
+//   32w .. 32w+31 of the tile and all 128 rows, as 4 tiles of
+//   v_mfma_f32_32x32x16_f16 (two waves per SIMD, so one wave's vector-ALU
+//   dequantization overlaps the other's matrix-core work).
 // * (K % 64 == 0; otherwise the register-staged kernel at the end of this
 //   file runs.) K advances 64 (two Q8_0 blocks) per step through a ring of NS LDS
 //   stages. Each stage holds the X tile (128 rows x 64 fp16) and the raw W
@@ -32,24 +33,25 @@ namespace lqmm {
 namespace {
 
 constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int NS = 4;                        // LDS stages of the X tile
 constexpr int kXStageBytes = BM * BK * 2;    // 16 KB
 constexpr int kXLoads = kXStageBytes / 16 / kThreads;  // 16-byte loads per thread per step
-// Raw W: each wave owns 64 rows of the tile. A step is 68 bytes of a row,
+// Raw W: each wave owns 32 rows of the tile. A step is 68 bytes of a row,
 // fetched as five 16-byte pieces at byte 0, 16, 32, 48 and 52 (the last two
 // overlap, so nothing past the row's step is read) and kept in the wave's
 // own LDS area as an 80-byte record per row, two steps deep.
-constexpr int kWRows = 64;                   // rows per wave
+constexpr int kWRows = BN / kWaves;          // rows per wave (32)
 constexpr int kWRec = 80;                    // LDS bytes per row record
 constexpr int kWPieces = 5;
-constexpr int kWLoads = kWRows * kWPieces / 64;  // 16-byte loads per lane per step
-constexpr int kWWaveBytes = 2 * kWRows * kWRec;  // per wave, two steps
-constexpr int kLdsBytes = NS * kXStageBytes + 4 * kWWaveBytes;
+constexpr int kWLoads = (kWRows * kWPieces + 63) / 64;  // 16-byte loads per lane per step
+constexpr int kWWaveBytes = 2 * kWRows * kWRec;         // per wave, two steps
+constexpr int kLdsBytes = NS * kXStageBytes + kWaves * kWWaveBytes;
 // Loads a wave issues per step (W to registers, X to LDS), as vmcnt counts
 // them.
 constexpr int kLoadsPerStep = kXLoads + kWLoads;
-static_assert(kXStageBytes % (16 * kThreads) == 0 && kWRows * kWPieces % 64 == 0, "");
+static_assert(kXStageBytes % (16 * kThreads) == 0, "");
 static_assert(NS >= 3 && (NS - 2) * kLoadsPerStep <= 63, "vmcnt range");
 
 // Slot of 16-byte chunk c (0..7) of X tile row r: chunks permuted per row
@@ -117,13 +119,17 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
     const int r = slot >> 3, c = xslot(r, slot & 7);  // slot & 7 holds chunk c of row r
     xoff[i] = (uint32_t)r * Ku * 2 + 16 * c;
   }
-  // W: piece p = 64 i + lane of this wave's 320 pieces: row p / 5, piece
-  // p % 5; it goes to byte 16 p of the wave's record area (80 bytes a row).
-  uint32_t woff[kWLoads];
+  // W: piece p = 64 i + lane of this wave's kWRows * 5 pieces (lanes past the
+  // last piece repeat it): row p / 5, piece p % 5, kept at byte 16 p of the
+  // wave's record area (80 bytes a row).
+  uint32_t woff[kWLoads], wdst[kWLoads];
 #pragma unroll
   for (int i = 0; i < kWLoads; ++i) {
-    const int p = 64 * i + lane, rr = p / kWPieces, k = p % kWPieces;
+    int p = 64 * i + lane;
+    p = p < kWRows * kWPieces ? p : kWRows * kWPieces - 1;
+    const int rr = p / kWPieces, k = p % kWPieces;
     woff[i] = (uint32_t)(wave * kWRows + rr) * row_bytes + (k < 4 ? 16 * k : 52);
+    wdst[i] = 16 * p;
   }
   uint8_t *const wl = smem + NS * kXStageBytes + wave * kWWaveBytes;  // this wave's W records
 
@@ -145,76 +151,68 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
   auto store_w = [&](const u32x4 (&rw)[kWLoads], int buf) {
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i)
-      *reinterpret_cast<u32x4 *>(wl + buf * (kWRows * kWRec) + 16 * (64 * i + lane)) = rw[i];
+      *reinterpret_cast<u32x4 *>(wl + buf * (kWRows * kWRec) + wdst[i]) = rw[i];
   };
 
-  // B operands of one step from this wave's W records: column group j
-  // (rows 32 j + l % 32 of the wave) and block h; slice s uses codes
-  // 8s .. 8s+7. Record layout: bytes 0..63 of the step at 0..63, bytes
-  // 52..67 at 64..79, so byte b >= 64 sits at b + 12. Block 0: d and codes
-  // in dwords 0..8 (codes 2 bytes in); block 1: d in the high half of
-  // dword 8, codes in dwords 9..15 and 19 (aligned).
-  // Raw reads of one step's records (column group j = 0, 1), and the
-  // dequantization of slice s from them.
-  struct Raw {
-    uint32_t q[2][9];
-    uint32_t d[2];
-  };
-  auto raw_read = [&](int buf, Raw &r) {
+  // B operands of one step from this wave's W records: this lane's column
+  // (row l % 32 of the wave) and block h; slice s uses codes 8s .. 8s+7.
+  // Record layout: bytes 0..63 of the step at 0..63, bytes 52..67 at
+  // 64..79, so byte b >= 64 sits at b + 12. Block 0: d and codes in dwords
+  // 0..8 (codes 2 bytes in); block 1: d in the high half of dword 8, codes
+  // in dwords 9..15 and 19 (aligned).
+  auto dequant_step = [&](int buf, half8_t (&b)[4]) {
+    const uint32_t *rw = reinterpret_cast<const uint32_t *>(wl + buf * (kWRows * kWRec) + l32 * kWRec);
+    const uint32_t dword = rw[8 * h];
+    uint32_t q[9];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t *rw =
-          reinterpret_cast<const uint32_t *>(wl + buf * (kWRows * kWRec) + (32 * j + l32) * kWRec);
-      r.d[j] = rw[8 * h];
-#pragma unroll
-      for (int i = 0; i < 7; ++i) r.q[j][i] = rw[9 * h + i];
-      r.q[j][7] = rw[7 + 12 * h];
-      r.q[j][8] = rw[8 + 11 * h];  // unused for block 1 (offset 0)
-    }
-  };
-  auto dequant_slice = [&](const Raw &r, int s, half8_t (&b)[2][4]) {
+    for (int i = 0; i < 7; ++i) q[i] = rw[9 * h + i];
+    q[7] = rw[7 + 12 * h];
+    q[8] = rw[8 + 11 * h];  // unused for block 1 (offset 0)
+    const half_t dh = __builtin_bit_cast(half_t, (uint16_t)__builtin_amdgcn_ubfe(dword, 16 * h, 16));
+    const half2_t d2 = {dh, dh};
     const uint32_t shift = 2 - 2 * h;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const half_t dh = __builtin_bit_cast(half_t, (uint16_t)__builtin_amdgcn_ubfe(r.d[j], 16 * h, 16));
-      const half2_t d2 = {dh, dh};
-      const uint32_t w0 = __builtin_amdgcn_alignbyte(r.q[j][2 * s + 1], r.q[j][2 * s], shift);
-      const uint32_t w1 = __builtin_amdgcn_alignbyte(r.q[j][2 * s + 2], r.q[j][2 * s + 1], shift);
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w0 = __builtin_amdgcn_alignbyte(q[2 * s + 1], q[2 * s], shift);
+      const uint32_t w1 = __builtin_amdgcn_alignbyte(q[2 * s + 2], q[2 * s + 1], shift);
       uint32_t p0, p1, p2, p3;
       dequant_word(w0, d2, p0, p1);
       dequant_word(w1, d2, p2, p3);
-      b[j][s] = __builtin_bit_cast(half8_t, u32x4{p0, p1, p2, p3});
+      b[s] = __builtin_bit_cast(half8_t, u32x4{p0, p1, p2, p3});
     }
   };
 
-  // Each wave owns a 128 x 64 block of the tile as 4 x 2 tiles of
+  // Each wave owns a 128 x 32 block of the tile as 4 tiles of
   // v_mfma_f32_32x32x16_f16: lane l supplies row (or column) l % 32 and the
-  // 8 k values 8 * (l / 32) .. +7 of each operand.
-  float16_t acc[4][2];
+  // 8 k values 8 * (l / 32) .. +7 of each operand. Two waves share each
+  // SIMD, so one wave's dequantization overlaps the other's MFMAs.
+  float16_t acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
+  // Pipeline. X: buffer-to-LDS loads NS - 1 steps ahead, shared by the
+  // workgroup (one barrier per step). W: each wave's own rows, loaded into
+  // registers two steps ahead and written to the wave's record buffer one
+  // step ahead (only this wave reads it, and one wave's LDS operations
+  // complete in order, so no barrier is needed). When step kt's X stage is
+  // read, the loads issued after it are W and X of the NS - 2 previous
+  // iterations; the prologue waits for all of its own loads.
   u32x4 rw[kWLoads];  // W step kt + 1 during iteration kt, then step kt + 2
-  // Iteration kt: write W step kt + 1 (in registers) to record buffer
-  // (kt + 1) & 1, request W step kt + 2 into the same registers and X step
-  // kt + NS - 1; then the MFMAs of step kt (B operands `cur`, dequantized in
-  // the previous iteration) with step kt + 1's dequantization (into `next`)
-  // interleaved, slice by slice, so that matrix-core and vector-ALU work
-  // overlap within the wave. When step kt's X stage is read, the loads
-  // issued after it are W and X of the NS - 2 previous iterations; the
-  // prologue waits for all of its own loads.
-  auto iteration = [&](int kt, const half8_t (&cur)[2][4], half8_t (&next)[2][4]) {
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue_x(s);
+  load_w(rw, 0);
+  store_w(rw, 0);
+  load_w(rw, 1);
+  for (int kt = 0; kt < nk; ++kt) {
     wait_and_barrier<(NS - 2) * kLoadsPerStep>();
     store_w(rw, (kt + 1) & 1);
     load_w(rw, kt + 2);
     issue_x(kt + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
-    Raw r;
-    raw_read((kt + 1) & 1, r);
+    half8_t b[4];
+    dequant_step(kt & 1, b);
     const uint8_t *st = smem + (kt % NS) * kXStageBytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -226,65 +224,22 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], cur[j][s], acc[i][j], 0, 0, 0);
-      dequant_slice(r, s, next);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[s], acc[i], 0, 0, 0);
     }
-    // Scheduling hint: the raw reads and the first A reads, then per slice
-    // eight MFMAs each followed by a few VALU instructions, with the next
-    // slice's A reads in between.
-    __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        if (m == 3 && s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      }
-    }
-  };
-
-  // Pipeline. X: buffer-to-LDS loads NS - 1 steps ahead, shared by the
-  // workgroup (one barrier per step). W: each wave's own rows, loaded into
-  // registers two steps ahead and written to the wave's record buffer one
-  // step ahead (only this wave reads it, and one wave's LDS operations
-  // complete in order, so no barrier is needed).
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue_x(s);
-  load_w(rw, 0);
-  store_w(rw, 0);
-  load_w(rw, 1);
-  half8_t b0[2][4], b1[2][4];
-  {
-    Raw r;
-    raw_read(0, r);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) dequant_slice(r, s, b0);
   }
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    iteration(kt, b0, b1);
-    iteration(kt + 1, b1, b0);
-  }
-  if (kt < nk) iteration(kt, b0, b1);
   // Drain the loads issued past the end before the workgroup exits.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // D layout of v_mfma_f32_32x32x16_f16: lane l holds column l % 32 and rows
   // 8 * (v / 4) + 4 * (l / 32) + v % 4 for v = 0..15.
+  const int64_t col = n0 + wave * 32 + l32;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wave * 64 + j * 32 + l32;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row < M && col < N)
-          Y[row * N + col] = __builtin_bit_cast(uint16_t, (half_t)acc[i][j][v]);
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (row < M && col < N)
+        Y[row * N + col] = __builtin_bit_cast(uint16_t, (half_t)acc[i][v]);
     }
 }
 
