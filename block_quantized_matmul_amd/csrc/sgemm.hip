@@ -5,8 +5,9 @@
 // shared-memory tiles, zero padding at ragged edges, two barriers around each
 // tile's use, guarded stores. The page's 16x16 scalar tiles are replaced by a
 // CDNA4 design:
-// * 128x128 output tile per 256-thread workgroup, four waves of 64x64, each
-//   wave a 4x4 grid of v_mfma_f32_16x16x4_f32 accumulators (fp32 products,
+// * 128x128 output tile per 512-thread workgroup, eight waves of 64x32
+//   (two per SIMD, so one wave's LDS reads overlap the other's MFMAs), each
+//   wave a 4x2 grid of v_mfma_f32_16x16x4_f32 accumulators (fp32 products,
 //   fp32 accumulation);
 // * K advances 32 at a time through two LDS buffers: the next tile's global
 //   loads are issued before the current tile's MFMAs, and one barrier per step
@@ -20,10 +21,13 @@
 namespace lqmm {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kKQ = BK / 4;  // float4 groups per A row
 constexpr int LDA = BK + 4;  // As row stride (floats)
 constexpr int LDB = BN + 4;  // Bs row stride (floats)
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kLoads = BM * BK / 4 / kThreads;  // float4 loads per thread per tile (A, and B)
+static_assert(BM * BK == BK * BN && BM * BK % (4 * kThreads) == 0, "");
 
 template <bool VEC>
 __device__ __forceinline__ float4_t load4_a(const float *__restrict__ A, int64_t M, int64_t K,
@@ -64,19 +68,19 @@ sgemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float *__
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 64 x 32
   const int li = lane & 15, lg = lane >> 4;
 
-  float4_t ra[4], rb[4];
+  float4_t ra[kLoads], rb[kLoads];
   auto load_tile = [&](int64_t k0) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kLoads; ++it) {
       int idx = tid + kThreads * it;
-      int row = idx >> 3, kq = idx & 7;
+      int row = idx / kKQ, kq = idx % kKQ;
       ra[it] = load4_a<VEC>(A, M, K, m0 + row, k0 + 4 * kq);
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kLoads; ++it) {
       int idx = tid + kThreads * it;
       int k = idx >> 5, jq = idx & 31;
       rb[it] = load4_b<VEC>(B, K, N, k0 + k, n0 + 4 * jq);
@@ -84,24 +88,24 @@ sgemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float *__
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kLoads; ++it) {
       int idx = tid + kThreads * it;
-      int row = idx >> 3, kq = idx & 7;
+      int row = idx / kKQ, kq = idx % kKQ;
       *reinterpret_cast<float4_t *>(&As[buf][row * LDA + 4 * kq]) = ra[it];
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kLoads; ++it) {
       int idx = tid + kThreads * it;
       int k = idx >> 5, jq = idx & 31;
       *reinterpret_cast<float4_t *>(&Bs[buf][k * LDB + 4 * jq]) = rb[it];
     }
   };
 
-  float4_t acc[4][4];
+  float4_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) acc[i][j] = float4_t{0, 0, 0, 0};
 
   const int64_t nk = (K + BK - 1) / BK;
   load_tile(0);
@@ -114,22 +118,22 @@ sgemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float *__
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       float4_t a[4];
-      float b[4][4];
+      float b[2][4];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti)
         a[ti] = *reinterpret_cast<const float4_t *>(
             &As[cur][(wm * 64 + ti * 16 + li) * LDA + kk * 16 + 4 * lg]);
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj)
+      for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          b[tj][s] = Bs[cur][(kk * 16 + 4 * lg + s) * LDB + wn * 64 + tj * 16 + li];
+          b[tj][s] = Bs[cur][(kk * 16 + 4 * lg + s) * LDB + wn * 32 + tj * 16 + li];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-          for (int tj = 0; tj < 4; ++tj)
+          for (int tj = 0; tj < 2; ++tj)
             acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ti][s], b[tj][s], acc[ti][tj],
                                                                 0, 0, 0);
     }
@@ -141,8 +145,8 @@ sgemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float *__
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      const int64_t col = n0 + wn * 64 + tj * 16 + li;
+    for (int tj = 0; tj < 2; ++tj) {
+      const int64_t col = n0 + wn * 32 + tj * 16 + li;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t row = m0 + wm * 64 + ti * 16 + 4 * lg + v;
