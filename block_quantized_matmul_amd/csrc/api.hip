@@ -106,16 +106,26 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
                                        ? env_u
                                        : (B <= 6 && N > 6 * 16 * (int64_t)num_cus ? 2 : 1))
                                 : 0;
+    // LDS beyond the staged activations: the coalesced kernel's per-wave
+    // weight staging areas (its k-split reduction reuses them), or the other
+    // MFMA kernel's reduction buffer.
     const int64_t red_bytes =
-        mfma ? (int64_t)lqmm::gemv_mfma_reduce_bytes(waves) +
-                   (lds_stage ? (int64_t)lqmm::gemv_coal_stage_bytes(lds_u) : 0)
-             : 0;
+        !mfma ? 0
+              : lds_stage ? (int64_t)lqmm::gemv_coal_stage_bytes(lds_u)
+                          : (int64_t)lqmm::gemv_mfma_reduce_bytes(waves);
     const int64_t lds_cap = lds_stage ? lqmm::kMaxLds : lqmm::kMaxGemvLds;
-    int64_t max_units = (lds_cap - red_bytes) / (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, 1);
+    // per-unit cost taken over many units, where the row padding is negligible
+    int64_t max_units =
+        (lds_cap - red_bytes) * 4096 / (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, 4096);
     // K-split launches start on whole Q4_K super-blocks, and on whole
     // super-chunks for the coalesced kernel.
-    if (fmt == GemvFormat::Q4_K) max_units &= ~(int64_t)3;
-    if (lds_stage) max_units -= max_units % sc_units;
+    const int64_t ustep = lds_stage ? sc_units : fmt == GemvFormat::Q4_K ? 4 : 1;
+    max_units -= max_units % ustep;
+    // the staged rows are padded: step back until they fit
+    while (max_units > ustep &&
+           (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, (int)max_units) + red_bytes > lds_cap)
+      max_units -= ustep;
+    if (max_units < ustep) return LQMM_ERR_SHAPE;
     for (int64_t u0 = 0; u0 < units_total; u0 += max_units) {
       const int64_t nu64 = units_total - u0 < max_units ? units_total - u0 : max_units;
       const int nu = (int)nu64;
@@ -157,7 +167,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         pl.ksplit = ks;
         pl.waves = waves;
         pl.lds_stage = lds_stage;
-        pl.depth = env_depth > 0 ? env_depth : 2;
+        pl.depth = (env_depth == 2 || env_depth == 3 || env_depth == 4 || env_depth == 6) ? env_depth : 2;
         const int teams = waves / ks;
         wg_needed = (tiles + teams - 1) / teams;
       } else {

@@ -128,7 +128,7 @@ struct FmtQ4_0 {
   }
   // u must index a staged unit; `valid` = 0 makes the unit contribute 0.
   template <int B, int R>
-  static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs,
+  static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
                                                  const float *sums, int u, int nu, bool valid,
                                                  const UnpackMasks &k, float (&acc)[R][B]) {
     float s[R][B];
@@ -142,7 +142,7 @@ struct FmtQ4_0 {
     for (int t = 0; t < kWords; ++t) {
       u32x4 X[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * nu + u];
+      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * xstride + u];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         Nibbles n = unpack_word(raw[r].q[t], k);
@@ -252,7 +252,7 @@ struct FmtQ4_K {
     sums[2 * idx + 1] = -1024.0f * shi;
   }
   template <int B, int R>
-  static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs,
+  static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
                                                  const float *sums, int u, int nu, bool valid,
                                                  const UnpackMasks &k, float (&acc)[R][B]) {
     float slo[R][B], shi[R][B], nsl[B], nsh[B];
@@ -270,7 +270,7 @@ struct FmtQ4_K {
     for (int t = 0; t < kWords; ++t) {
       u32x4 X[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * nu + u];
+      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * xstride + u];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         Nibbles n = unpack_word(word(raw[r], t), k);
@@ -386,27 +386,41 @@ __device__ __forceinline__ u32x4 pack_xword(const XWord &w, float hi_scale) {
   return word;
 }
 
-// Stage words 0 .. total-1 into xs; `coords(i, b, u, t)` names word i. Each
-// thread keeps kBatch words' loads in flight (clamped indices, so the loads
-// are unconditional and the compiler waits once per batch, not once per
-// word).
-template <class F, int kThreads, int kBatch, class Coords>
-__device__ __forceinline__ void stage_words(u32x4 *xs, int total, const float *__restrict__ x,
-                                            int64_t ldx, float hi_scale, Coords coords) {
+// Staged words are grouped by word index t: word t of every (row, unit) pair
+// lies in a block of `stride` slots. The stride is padded to 16/T modulo 16
+// slots (T words per unit), so that the T lanes that stage the words of one
+// (row, unit) pair write to distinct LDS banks.
+template <class F>
+__host__ __device__ __forceinline__ int staged_stride(int n) {
+  return ((n + 15) & ~15) + 16 / F::kWords;
+}
+
+// Stage the words of batch rows 0..nb-1 and units 0..nu-1 into xs, word
+// (b, u, t) at slot(b, u, t). Threads take the words in (t, b, u) order, t
+// fastest, so T neighbouring lanes read the contiguous activations of one
+// (row, unit) pair and the global loads are coalesced. Each thread keeps
+// kBatch words' loads in flight (clamped indices, so the loads are
+// unconditional and the compiler waits once per batch, not once per word).
+template <class F, int kThreads, int kBatch, class Slot>
+__device__ __forceinline__ void stage_words(u32x4 *xs, int nb, int nu, const float *__restrict__ x,
+                                            int64_t ldx, float hi_scale, Slot slot) {
+  constexpr int T = F::kWords;
+  const int total = nb * nu * T;
   for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
     XWord w[kBatch];
+    int dst[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = base + k * kThreads;
-      int b, u, t;
-      coords(i < total ? i : total - 1, b, u, t);
+      const int ic = i < total ? i : total - 1;
+      const int t = ic % T, r = ic / T;
+      const int b = r % nb, u = r / nb;
       w[k] = load_xword<F>(x, ldx, b, u, t);
+      dst[k] = i < total ? slot(b, u, t) : -1;
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = base + k * kThreads;
-      if (i < total) xs[i] = pack_xword(w[k], hi_scale);
-    }
+    for (int k = 0; k < kBatch; ++k)
+      if (dst[k] >= 0) xs[dst[k]] = pack_xword(w[k], hi_scale);
   }
 }
 
@@ -431,8 +445,9 @@ gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int
             int64_t N, int lpr_log2_arg, int accumulate) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int T = F::kWords;
-  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);
-  float *sums = reinterpret_cast<float *>(smem + (size_t)B * T * nu * 16);
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (b*T + t)*NS + u
+  const int NS = staged_stride<F>(nu);
+  float *sums = reinterpret_cast<float *>(smem + (size_t)B * T * NS * 16);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -471,19 +486,16 @@ gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int
   int c = 0;
   load(buf0, g < ngroups ? g : ngroups - 1, 0);
 
-  // Stage: slot (b*T + t)*nu + u, u fastest; then the per-(b, u) sums.
+  // Stage the words, then the per-(b, u) sums.
   // (one or two words per thread at batch 1 and 2: no batching)
-  stage_words<F, kGemvThreads, 1>(xs, B * T * nu, x, ldx, 0.0625f, [&](int i, int &b, int &u, int &t) {
-    u = i % nu;
-    b = i / nu / T;
-    t = i / nu % T;
-  });
+  stage_words<F, kGemvThreads, 1>(xs, B, nu, x, ldx, 0.0625f,
+                                  [&](int b, int u, int t) { return (b * T + t) * NS + u; });
   __syncthreads();
   for (int i = tid; i < B * nu; i += kGemvThreads) {
     const int u = i % nu, b = i / nu;
     float slo = 0.0f, shi = 0.0f;
 #pragma unroll
-    for (int t = 0; t < T; ++t) word_sums(xs[(b * T + t) * nu + u], slo, shi);
+    for (int t = 0; t < T; ++t) word_sums(xs[(b * T + t) * NS + u], slo, shi);
     F::stage_sums(sums, i, slo, shi);
   }
   __syncthreads();
@@ -512,7 +524,7 @@ gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int
       typename F::Raw one[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) one[r] = src[r][j];
-      F::template compute<B, R>(one, xs, sums, u < nu ? u : nu - 1, nu, u < nu, kmask, acc);
+      F::template compute<B, R>(one, xs, NS, sums, u < nu ? u : nu - 1, nu, u < nu, kmask, acc);
     }
     if (c == nchunks - 1) {
 #pragma unroll
@@ -571,8 +583,9 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   constexpr int T = F::kWords;
   constexpr int kThreads = NW * kWave;
   constexpr int kTeams = NW / KS;
-  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (t*nu + u)*nb + b
-  float4_t *red = reinterpret_cast<float4_t *>(smem + (size_t)nb * T * nu * 16);
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot t*TS + u*nb + b
+  const int TS = staged_stride<F>(nu * nb);
+  float4_t *red = reinterpret_cast<float4_t *>(smem + (size_t)T * TS * 16);
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -622,11 +635,8 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   int c = 0;
   load(buf0, gb + team, 0);
 
-  stage_words<F, kThreads, 4>(xs, nb * T * nu, x, ldx, 1.0f, [&](int i, int &b, int &u, int &t) {
-    b = i % nb;
-    u = i / nb % nu;
-    t = i / nb / nu;
-  });
+  stage_words<F, kThreads, 4>(xs, nb, nu, x, ldx, 1.0f,
+                              [&](int b, int u, int t) { return t * TS + u * nb + b; });
   __syncthreads();
 
   const UnpackMasks kmask;
@@ -659,7 +669,7 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
       for (int r = 0; r < R; ++r) pr[r] = F::prep(src[r][j], ux & 3, valid);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const half8_t a = __builtin_bit_cast(half8_t, xrow[t * nu * nb]);
+        const half8_t a = __builtin_bit_cast(half8_t, xrow[t * TS]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(src[r][j], pr[r], t, kmask));
@@ -787,8 +797,10 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   constexpr int NI = (NP + 63) / 64;  // loads per lane per chunk
   constexpr int UPC = U * C::kUnitsPerSC;  // units per chunk
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (t*nu + u)*nb + b
-  float4_t *red = reinterpret_cast<float4_t *>(smem + (size_t)nb * T * nu * 16);
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot t*TS + u*nb + b
+  const int TS = staged_stride<F>(nu * nb);
+  // Per-wave weight staging areas; the k-split reduction reuses them.
+  u32x4 *wbase = reinterpret_cast<u32x4 *>(smem + (size_t)T * TS * 16);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -796,8 +808,8 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   const int lane = tid & (kWave - 1);
   const int n = lane & 15;
   const int q = lane >> 4;
-  u32x4 *wbuf = reinterpret_cast<u32x4 *>(smem + (size_t)nb * T * nu * 16 + NW * kWave * 16) +
-                wave * NI * kWave;
+  u32x4 *wbuf = wbase + wave * NI * kWave;
+  auto red = [&](int w) { return reinterpret_cast<float4_t *>(wbase + w * NI * kWave) + lane; };
   const int ngroups = (int)((N + 15) / 16);
   // Units per slice, a whole number of chunks; every slice runs the same
   // number of chunks (units past the end of its range are zeroed).
@@ -854,11 +866,8 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
     advance(pg, pc);
   }
 
-  stage_words<F, kGemvThreads, 4>(xs, nb * T * nu, x, ldx, 1.0f, [&](int i, int &b, int &u, int &t) {
-    b = i % nb;
-    u = i / nb % nu;
-    t = i / nb / nu;
-  });
+  stage_words<F, kGemvThreads, 4>(xs, nb, nu, x, ldx, 1.0f,
+                                  [&](int b, int u, int t) { return t * TS + u * nb + b; });
   __syncthreads();
 
   const UnpackMasks kmask;
@@ -877,32 +886,54 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
     advance(pg, pc);
     const int nominal = ubeg + cc * UPC;
     const int ustart = chunk_start(cc);
+    // All LDS reads of the chunk (activations, then the lane's weight units)
+    // are issued together, so the wave waits for LDS once per chunk rather
+    // than before every MFMA.
+    constexpr int LU = U * C::kLaneUnits;
+    u32x4 xa[LU][T];
+    typename F::Raw rw[LU];
+#pragma unroll
+    for (int s = 0; s < U; ++s)
+#pragma unroll
+      for (int j = 0; j < C::kLaneUnits; ++j) {
+        const int u = ustart + s * C::kUnitsPerSC + q * C::kLaneUnits + j;
+        const u32x4 *xrow = xs + u * nb + xb;
+#pragma unroll
+        for (int t = 0; t < T; ++t) xa[s * C::kLaneUnits + j][t] = xrow[t * TS];
+      }
+#pragma unroll
+    for (int s = 0; s < U; ++s)
+#pragma unroll
+      for (int j = 0; j < C::kLaneUnits; ++j)
+        rw[s * C::kLaneUnits + j] = C::read(wbuf + n * PR + 9 * s, q, j);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < U; ++s) {
-      const u32x4 *sc = wbuf + n * PR + 9 * s;
 #pragma unroll
       for (int j = 0; j < C::kLaneUnits; ++j) {
         const int ul = s * C::kUnitsPerSC + q * C::kLaneUnits + j;  // unit within the chunk
         const int u = ustart + ul;
         const bool valid = u >= nominal && u < uend;
-        const typename F::Raw r = C::read(sc, q, j);
+        const typename F::Raw &r = rw[s * C::kLaneUnits + j];
         const typename F::Prep pr = F::prep(r, q, valid);
-        const u32x4 *xrow = xs + u * nb + xb;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const half8_t a = __builtin_bit_cast(half8_t, xrow[t * nu * nb]);
+          const half8_t a = __builtin_bit_cast(half8_t, xa[s * C::kLaneUnits + j][t]);
           const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(r, pr, t, kmask));
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wv, acc, 0, 0, 0);
         }
       }
     }
     if (cc == nchunks - 1) {
+      // The wave's own staging area is free once its chunk is computed (one
+      // wave's LDS operations complete in order); the closing barrier keeps
+      // the next chunk's staging writes behind the slice-0 wave's reads.
       if (KS > 1) {
-        red[wave * kWave + lane] = acc;
+        *red(wave) = acc;
         __syncthreads();
         if (slice == 0) {
 #pragma unroll
-          for (int s2 = 1; s2 < KS; ++s2) acc += red[(wave + s2) * kWave + lane];
+          for (int s2 = 1; s2 < KS; ++s2) acc += *red(wave + s2);
         }
       }
       const int g = cg + team;
@@ -974,25 +1005,33 @@ hipError_t launch_coal(const GemvPlan &pl, const uint8_t *W, const float *x, flo
   return hipGetLastError();
 }
 
-// Coalesced-kernel instances: U in {1, 2}, KS in {1, 2, 4, 8}, depth 2 (3 for
-// tuning sweeps).
+// Coalesced-kernel instances: U in {1, 2}, KS in {1, 2, 4, 8}, depth 2, 3, 4
+// or 6 chunks in flight per wave.
+template <class C, int U, int D>
+hipError_t launch_coal_ks(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                          hipStream_t s) {
+  switch (pl.ksplit) {
+    case 1: return launch_coal<C, U, 1, D>(pl, W, x, y, s);
+    case 2: return launch_coal<C, U, 2, D>(pl, W, x, y, s);
+    case 4: return launch_coal<C, U, 4, D>(pl, W, x, y, s);
+    default: return launch_coal<C, U, 8, D>(pl, W, x, y, s);
+  }
+}
+template <class C, int U>
+hipError_t launch_coal_d(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                         hipStream_t s) {
+  switch (pl.depth) {
+    case 2: return launch_coal_ks<C, U, 2>(pl, W, x, y, s);
+    case 3: return launch_coal_ks<C, U, 3>(pl, W, x, y, s);
+    case 4: return launch_coal_ks<C, U, 4>(pl, W, x, y, s);
+    default: return launch_coal_ks<C, U, 6>(pl, W, x, y, s);
+  }
+}
 template <class C>
 hipError_t launch_coal_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                            hipStream_t s) {
-#define LQMM_COAL(UU, DD)                                                    \
-  switch (pl.ksplit) {                                                       \
-    case 1: return launch_coal<C, UU, 1, DD>(pl, W, x, y, s);                \
-    case 2: return launch_coal<C, UU, 2, DD>(pl, W, x, y, s);                \
-    case 4: return launch_coal<C, UU, 4, DD>(pl, W, x, y, s);                \
-    default: return launch_coal<C, UU, 8, DD>(pl, W, x, y, s);               \
-  }
-  if (pl.units_per_lane == 2) {
-    if (pl.depth >= 3) { LQMM_COAL(2, 3) }
-    LQMM_COAL(2, 2)
-  }
-  if (pl.depth >= 3) { LQMM_COAL(1, 3) }
-  LQMM_COAL(1, 2)
-#undef LQMM_COAL
+  if (pl.units_per_lane == 2) return launch_coal_d<C, 2>(pl, W, x, y, s);
+  return launch_coal_d<C, 1>(pl, W, x, y, s);
 }
 
 template <class F, int R, int U, int KS, int NW>
@@ -1060,10 +1099,15 @@ hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, floa
 
 }  // namespace
 
+template <class F>
+size_t staged_bytes(bool mfma, int batch, int nu) {
+  if (mfma) return (size_t)F::kWords * staged_stride<F>(nu * batch) * 16;
+  return (size_t)batch * F::kWords * staged_stride<F>(nu) * 16 + (size_t)batch * nu * F::kSums * 4;
+}
+
 size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu) {
-  const int words = f == GemvFormat::Q4_0 ? FmtQ4_0::kWords : FmtQ4_K::kWords;
-  const int sums = f == GemvFormat::Q4_0 ? FmtQ4_0::kSums : FmtQ4_K::kSums;
-  return (size_t)batch * nu * (words * 16 + (mfma ? 0 : sums * 4));
+  return f == GemvFormat::Q4_0 ? staged_bytes<FmtQ4_0>(mfma, batch, nu)
+                               : staged_bytes<FmtQ4_K>(mfma, batch, nu);
 }
 
 size_t gemv_mfma_reduce_bytes(int waves) { return (size_t)waves * kWave * 16; }
