@@ -53,7 +53,10 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # The GPU raises its clocks over the first tens of milliseconds of
+    # sustained work; 100 untimed steps (about 40 ms) reach the steady state
+    # that a serving loop runs in.
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")

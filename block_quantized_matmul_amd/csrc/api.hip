@@ -150,10 +150,24 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         int uu = lds_stage ? lds_u : 2, ks = waves == 16 ? 4 : 1;
         const int ksmax = waves == 16 ? 16 : 8;
         while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
-        // Coalesced kernel: all eight waves on one tile (eight K-slices) up
-        // to three tiles per CU; fewer, longer slices for larger N (measured
-        // on N = 4096 .. 28672, K = 4096 and 8192, batch 3 to 8).
-        if (lds_stage) ks = tiles <= 3 * (int64_t)num_cus ? 8 : tiles <= 6 * (int64_t)num_cus ? 2 : 1;
+        // Coalesced kernel (one workgroup per CU): the number of K-slices per
+        // tile that gives each wave the fewest units, counting the last,
+        // partly filled pass of workgroups over the CUs as a whole one; ties
+        // go to more slices.
+        if (lds_stage) {
+          int64_t best = -1;
+          for (int k = 8; k >= 1; k /= 2) {
+            const int64_t wgs = (tiles * k + 7) / 8;
+            const int64_t grid_k = wgs < (int64_t)num_cus * wg_per_cu ? wgs : (int64_t)num_cus * wg_per_cu;
+            const int64_t upc = (int64_t)sc_units * uu;  // units per chunk
+            const int64_t slice = ((nu + k - 1) / k + upc - 1) / upc * upc;
+            const int64_t cost = (wgs + grid_k - 1) / grid_k * slice;
+            if (best < 0 || cost < best) {
+              best = cost;
+              ks = k;
+            }
+          }
+        }
         if (!lds_stage && (env_u == 2 || env_u == 4)) uu = env_u;
         if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
           ks = env_ks;
