@@ -6,53 +6,61 @@
 // into shared memory (the CU's LDS), dequantized and reused by every row of
 // the M tile.
 //
-// * One 512-thread workgroup per 128 x 256 output tile; wave w owns columns
-//   32w .. 32w+31 of the tile and all 128 rows, as 4 tiles of
-//   v_mfma_f32_32x32x16_f16 (two waves per SIMD, so one wave's vector-ALU
-//   dequantization overlaps the other's matrix-core work).
+// * One workgroup of NWAVES waves (8, or 7 when that tiles the GPU better)
+//   per 128 x (32 * NWAVES) output tile; wave w owns columns 32w .. 32w+31
+//   of the tile and all 128 rows, as 4 tiles of v_mfma_f32_32x32x16_f16 (two
+//   waves per SIMD, so one wave's vector-ALU dequantization overlaps the
+//   other's matrix-core work).
 // * (K % 64 == 0; otherwise the register-staged kernel at the end of this
-//   file runs.) K advances 64 (two Q8_0 blocks) per step through a ring of NS LDS
-//   stages. Each stage holds the X tile (128 rows x 64 fp16) and the raw W
-//   tile (256 rows x 68 bytes: both blocks of every row, as stored), both
-//   written by buffer-to-LDS loads issued NS - 1 steps ahead. Raw Q8_0 bytes
-//   in LDS cost about half the LDS write bandwidth of dequantized fp16, and
-//   LDS writes run at about half the rate of LDS reads on this GPU.
-// * Each wave dequantizes its own columns once per step, from LDS straight
-//   into MFMA B operands (so each weight is dequantized once per workgroup
-//   and reused by all 128 rows): q ^ 0x80 placed in the mantissa of 1024.0
-//   with v_perm_b32 is exactly 1152 + q; a packed subtract gives q and a
-//   packed multiply gives fp16(d*q), one rounding.
+//   file runs.) K advances 64 (two Q8_0 blocks) per step. The X tile (128
+//   rows x 64 fp16) goes through a ring of NS LDS stages, written by
+//   buffer-to-LDS loads issued NS - 1 steps ahead and shared by the
+//   workgroup. Each wave loads the raw Q8_0 bytes of its own 32 weight rows
+//   into registers two steps ahead and keeps them in its own LDS records one
+//   step ahead: raw bytes cost about half the LDS write bandwidth of
+//   dequantized fp16, and LDS writes run at about half the rate of LDS reads
+//   on this GPU.
+// * Each wave dequantizes its own columns once per step, from its records
+//   straight into MFMA B operands (so each weight is dequantized once per
+//   workgroup and reused by all 128 rows): q ^ 0x80 placed in the mantissa
+//   of 1024.0 with v_perm_b32 is exactly 1152 + q; a packed subtract gives q
+//   and a packed multiply gives fp16(d*q), one rounding.
 // * K order inside a step: MFMA slice s (16 k) takes, in lane half h, the
 //   codes 8s .. 8s+7 of block h. A operands (X) are read in the same order;
 //   the X tile is stored with 16-byte chunks permuted per row pair so that
 //   those reads are free of LDS bank conflicts.
+#include <stdlib.h>
+
 #include "lqmm_device.hpp"
 #include "lqmm_internal.hpp"
 
 namespace lqmm {
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+constexpr int BM = 128, BK = 64;
 constexpr int NS = 4;                        // LDS stages of the X tile
 constexpr int kXStageBytes = BM * BK * 2;    // 16 KB
-constexpr int kXLoads = kXStageBytes / 16 / kThreads;  // 16-byte loads per thread per step
+constexpr int kXInstr = kXStageBytes / 1024;  // buffer-to-LDS loads per stage (1 KB each)
 // Raw W: each wave owns 32 rows of the tile. A step is 68 bytes of a row,
 // fetched as five 16-byte pieces at byte 0, 16, 32, 48 and 52 (the last two
 // overlap, so nothing past the row's step is read) and kept in the wave's
 // own LDS area as an 80-byte record per row, two steps deep.
-constexpr int kWRows = BN / kWaves;          // rows per wave (32)
+constexpr int kWRows = 32;                   // weight rows per wave
 constexpr int kWRec = 80;                    // LDS bytes per row record
 constexpr int kWPieces = 5;
 constexpr int kWLoads = (kWRows * kWPieces + 63) / 64;  // 16-byte loads per lane per step
 constexpr int kWWaveBytes = 2 * kWRows * kWRec;         // per wave, two steps
-constexpr int kLdsBytes = NS * kXStageBytes + kWaves * kWWaveBytes;
-// Loads a wave issues per step (W to registers, X to LDS), as vmcnt counts
-// them.
-constexpr int kLoadsPerStep = kXLoads + kWLoads;
-static_assert(kXStageBytes % (16 * kThreads) == 0, "");
-static_assert(NS >= 3 && (NS - 2) * kLoadsPerStep <= 63, "vmcnt range");
+
+template <int NWAVES>
+struct Tile {
+  static constexpr int BN = kWRows * NWAVES;
+  static constexpr int kThreads = 64 * NWAVES;
+  // X loads per wave per step: wave w issues loads w, w + NWAVES, ... of the
+  // stage's kXInstr, so the first kXInstr % NWAVES waves issue one more.
+  static constexpr int kXMax = (kXInstr + NWAVES - 1) / NWAVES;
+  static constexpr int kLdsBytes = NS * kXStageBytes + NWAVES * kWWaveBytes;
+  static_assert(NS >= 3 && (NS - 2) * (kXMax + kWLoads) <= 63, "vmcnt range");
+};
 
 // Slot of 16-byte chunk c (0..7) of X tile row r: chunks permuted per row
 // pair, so that the 16 rows one ds_read_b128 phase touches hit 16 distinct
@@ -76,9 +84,13 @@ __device__ __forceinline__ void dequant_word(uint32_t w, half2_t d2, uint32_t &l
   hi = as_u32((h - bias) * d2);
 }
 
-__global__ void __launch_bounds__(kThreads)
+template <int NWAVES>
+__global__ void __launch_bounds__(64 * NWAVES)
 gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
                  uint16_t *__restrict__ Y, int64_t M, int64_t N, int64_t K, int tiles_n) {
+  using TT = Tile<NWAVES>;
+  constexpr int BN = TT::BN;
+  constexpr int kXMax = TT::kXMax;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -110,12 +122,14 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
   // Per-lane source offsets within the tile (VGPRs); the step's offset goes
   // in the scalar offset. Every byte a step reads lies inside its own row
   // (K % 64 == 0), and rows past M or N start past the end of the resource.
-  // X: buffer-to-LDS load i of wave w fills 64 consecutive 16-byte slots of
-  // the stage; lane L fills slot L.
-  uint32_t xoff[kXLoads];
+  // X: buffer-to-LDS load j = wave + i * NWAVES (j < kXInstr) fills 64
+  // consecutive 16-byte slots of the stage; lane L fills slot L.
+  const int nx = (kXInstr - wave + NWAVES - 1) / NWAVES;  // this wave's X loads per step
+  uint32_t xoff[kXMax];
 #pragma unroll
-  for (int i = 0; i < kXLoads; ++i) {
-    const int slot = (wave * kXLoads + i) * 64 + lane;
+  for (int i = 0; i < kXMax; ++i) {
+    const int j = wave + i * NWAVES;
+    const int slot = (j < kXInstr ? j : 0) * 64 + lane;
     const int r = slot >> 3, c = xslot(r, slot & 7);  // slot & 7 holds chunk c of row r
     xoff[i] = (uint32_t)r * Ku * 2 + 16 * c;
   }
@@ -133,13 +147,16 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
   }
   uint8_t *const wl = smem + NS * kXStageBytes + wave * kWWaveBytes;  // this wave's W records
 
+  // This wave's X loads of step kt (the test is wave-uniform, and absent
+  // when every wave issues kXMax).
   auto issue_x = [&](int kt) {
     const int ks = kt < nk ? kt : nk - 1;  // past the end: reload the last step, never read
     uint8_t *st = smem + (kt % NS) * kXStageBytes;
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (wave * kXLoads + i) * 1024, 16,
-                                               (int)xoff[i], ks * (BK * 2), 0, 0);
+    for (int i = 0; i < kXMax; ++i)
+      if (kXInstr % NWAVES == 0 || i < nx)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (wave + i * NWAVES) * 1024, 16,
+                                                 (int)xoff[i], ks * (BK * 2), 0, 0);
   };
   auto load_w = [&](u32x4 (&rw)[kWLoads], int kt) {
     const int ks = kt < nk ? kt : nk - 1;
@@ -194,21 +211,32 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
 
   // Pipeline. X: buffer-to-LDS loads NS - 1 steps ahead, shared by the
   // workgroup (one barrier per step). W: each wave's own rows, loaded into
-  // registers two steps ahead and written to the wave's record buffer one
-  // step ahead (only this wave reads it, and one wave's LDS operations
-  // complete in order, so no barrier is needed). When step kt's X stage is
-  // read, the loads issued after it are W and X of the NS - 2 previous
-  // iterations; the prologue waits for all of its own loads.
-  u32x4 rw[kWLoads];  // W step kt + 1 during iteration kt, then step kt + 2
+  // registers three steps ahead (two register sets) and written to the
+  // wave's record buffer one step ahead (only this wave reads it, and one
+  // wave's LDS operations complete in order, so no barrier is needed).
+  // Vector-memory loads complete in issue order, so waiting for a register
+  // load also waits for every older load; the register set consumed in step
+  // kt was loaded two iterations earlier, so that this wait leaves the X
+  // loads of the last two iterations in flight. Each iteration issues its W
+  // loads, then its X loads: when step kt's X stage is read, the loads
+  // issued after it are those of the NS - 2 later iterations; the prologue
+  // waits for all of its own loads.
+  u32x4 rw0[kWLoads], rw1[kWLoads];  // W of odd steps in rw1, even steps in rw0
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue_x(s);
-  load_w(rw, 0);
-  store_w(rw, 0);
-  load_w(rw, 1);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_and_barrier<(NS - 2) * kLoadsPerStep>();
-    store_w(rw, (kt + 1) & 1);
-    load_w(rw, kt + 2);
+  load_w(rw0, 0);
+  store_w(rw0, 0);
+  load_w(rw1, 1);
+  load_w(rw0, 2);
+  // Step kt: `cur` holds W of step kt + 1 and is refilled with step kt + 3.
+  auto step = [&](int kt, u32x4 (&cur)[kWLoads]) {
+    if (kXInstr % NWAVES == 0 || nx == kXMax)
+      wait_and_barrier<(NS - 2) * (kXMax + kWLoads)>();
+    else
+      wait_and_barrier<(NS - 2) * (kXMax - 1 + kWLoads)>();
+    store_w(cur, (kt + 1) & 1);
+    load_w(cur, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);  // keep the W loads ahead of the X loads
     issue_x(kt + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
     half8_t b[4];
@@ -226,7 +254,13 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
       for (int i = 0; i < 4; ++i)
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[s], acc[i], 0, 0, 0);
     }
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, rw1);
+    step(kt + 1, rw0);
   }
+  if (kt < nk) step(kt, rw1);
   // Drain the loads issued past the end before the workgroup exits.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -439,11 +473,39 @@ gemm_q8_0_k32_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__
 
 }  // namespace k32
 
+template <int NWAVES>
+hipError_t launch_fast(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M, int64_t N,
+                       int64_t K, hipStream_t stream) {
+  using TT = Tile<NWAVES>;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + TT::BN - 1) / TT::BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  // Load offsets (and the out-of-range marker 2^31) must fit in 31 bits.
+  if (tiles > 0x7fffffff || (int64_t)BM * K * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)TT::BN * (K / 32 * 34) >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_q8_0_kernel<NWAVES>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       TT::kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(gemm_q8_0_kernel<NWAVES>, dim3((unsigned)tiles), dim3(TT::kThreads),
+                     TT::kLdsBytes, stream, W, X, Y, M, N, K, (int)tiles_n);
+  return hipGetLastError();
+}
+
+// Tuning override for sweeps: LQMM_TUNE_GEMM_WAVES = 7 or 8.
+int env_waves_override() {
+  const char *s = getenv("LQMM_TUNE_GEMM_WAVES");
+  return s && *s ? atoi(s) : -1;
+}
+
 }  // namespace
 
 hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,
                             int64_t N, int64_t K, int num_cus, hipStream_t stream) {
-  (void)num_cus;
   if (K % 64 != 0) {
     const int64_t tiles_m = (M + k32::BM - 1) / k32::BM, tiles_n = (N + k32::BN - 1) / k32::BN;
     const int64_t tiles = tiles_m * tiles_n;
@@ -453,23 +515,19 @@ hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, in
                        stream, W, X, Y, M, N, K, (int)tiles_n);
     return hipGetLastError();
   }
-  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int64_t tiles = tiles_m * tiles_n;
-  // Load offsets (and the out-of-range marker 2^31) must fit in 31 bits.
-  if (tiles > 0x7fffffff || (int64_t)BM * K * 2 >= ((int64_t)1 << 31) ||
-      (int64_t)BN * (K / 32 * 34) >= ((int64_t)1 << 31))
-    return hipErrorInvalidValue;
-  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_q8_0_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipLaunchKernelGGL(gemm_q8_0_kernel, dim3((unsigned)tiles), dim3(kThreads), kLdsBytes,
-                     stream, W, X, Y, M, N, K, (int)tiles_n);
-  return hipGetLastError();
+  // Eight waves (128 x 256 tiles), or seven (128 x 224) when that takes
+  // fewer waves' worth of work per CU, counting a partly filled last pass of
+  // tiles over the CUs as a whole one (512 x 14336: 224 tiles of 256
+  // columns leave 32 CUs idle, 256 tiles of 224 columns fill all of them).
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t cus = num_cus > 0 ? num_cus : 1;
+  auto cost = [&](int64_t bn, int64_t waves) {
+    const int64_t t = tiles_m * ((N + bn - 1) / bn);
+    return (t + cus - 1) / cus * waves;
+  };
+  const int env_w = env_waves_override();
+  const bool seven = env_w == 7 || (env_w != 8 && cost(Tile<7>::BN, 7) < cost(Tile<8>::BN, 8));
+  return seven ? launch_fast<7>(W, X, Y, M, N, K, stream) : launch_fast<8>(W, X, Y, M, N, K, stream);
 }
 
 }  // namespace lqmm

@@ -211,7 +211,7 @@ def test_q4_k_extreme_codes(orc):
 # ------------------------------------------------------------- Q8_0 GEMM
 Q8_0_SMALL = [(1, 1, 32), (3, 5, 64), (17, 130, 96), (128, 128, 64), (130, 257, 320),
               (64, 200, 4096), (256, 512, 1024), (1, 300, 32),
-              # ragged in every dimension at once: partial 128 x 256 tiles and a
+              # ragged in every dimension at once: partial output tiles and a
               # last K step holding a single block
               (129, 257, 160), (300, 513, 224), (512, 768, 4128)]
 
@@ -223,6 +223,19 @@ def test_q8_0_small(orc, M, N, K):
     Y = host(bq.lqmm_gemm_q8_0_f16(dev(c.W.reshape(-1)), dev(c.X), N)).astype(np.float64)
     ref = orc.gemm_q8_0_f16(c.W, c.X, N, K)
     assert_close(Y, ref, TOL_QUANT, f"q8_0 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("waves", [7, 8])
+@pytest.mark.parametrize("M,N,K", [(300, 513, 224), (129, 481, 4096), (512, 1000, 128)])
+def test_q8_0_tile_widths(orc, monkeypatch, waves, M, N, K):
+    # the K % 64 == 0 kernel in both of its tile widths (224 and 256 columns),
+    # forced through the planner's tuning override
+    monkeypatch.setenv("LQMM_TUNE_GEMM_WAVES", str(waves))
+    c = synth.q8_0_case(M, N, K, seed=M + N + K + waves)
+    announce(f"q8_0 gemm M={M} N={N} K={K} waves={waves}")
+    Y = host(bq.lqmm_gemm_q8_0_f16(dev(c.W.reshape(-1)), dev(c.X), N)).astype(np.float64)
+    ref = orc.gemm_q8_0_f16(c.W, c.X, N, K)
+    assert_close(Y, ref, TOL_QUANT, f"q8_0 {M}x{N}x{K} waves={waves}")
 
 
 def test_q8_0_config_sampled(orc):
