@@ -957,13 +957,20 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
     advance(cg, cc);
   };
 
-  while (cg < ngroups) {
+  // Whole rounds of D stages, then the remainder: a loop without an early
+  // exit between the stages lets the compiler's load-counter waits keep the
+  // other buffers' loads in flight (with an exit between them it drained
+  // every load once per round).
+  const int gfirst = blockIdx.x * kTeams;
+  const int n_items = (ngroups - gfirst + group_stride - 1) / group_stride * nchunks;
+  int it = 0;
+  for (; it + D <= n_items; it += D) {
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-      stage(bufs[k]);
-      if (cg >= ngroups) break;
-    }
+    for (int k = 0; k < D; ++k) stage(bufs[k]);
   }
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k)
+    if (it + k < n_items) stage(bufs[k]);
 }
 
 template <class K>
