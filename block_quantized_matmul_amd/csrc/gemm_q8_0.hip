@@ -6,8 +6,8 @@
 // into shared memory (the CU's LDS), dequantized and reused by every row of
 // the M tile.
 //
-// * One workgroup of NWAVES waves (8, or 7 when that tiles the GPU better)
-//   per 128 x (32 * NWAVES) output tile; wave w owns columns 32w .. 32w+31
+// * One workgroup of NWAVES waves (8; 7 as a tuning override) per
+//   128 x (32 * NWAVES) output tile; wave w owns columns 32w .. 32w+31
 //   of the tile and all 128 rows, as 4 tiles of v_mfma_f32_32x32x16_f16 (two
 //   waves per SIMD, so one wave's vector-ALU dequantization overlaps the
 //   other's matrix-core work).
@@ -15,9 +15,9 @@
 //   file runs.) K advances 64 (two Q8_0 blocks) per step. The X tile (128
 //   rows x 64 fp16) goes through a ring of NS LDS stages, written by
 //   buffer-to-LDS loads issued NS - 1 steps ahead and shared by the
-//   workgroup. Each wave loads the raw Q8_0 bytes of its own 32 weight rows
-//   into registers two steps ahead and keeps them in its own LDS records one
-//   step ahead: raw bytes cost about half the LDS write bandwidth of
+//   workgroup. Each wave brings the raw Q8_0 bytes of its own 32 weight rows
+//   into its own LDS records with buffer-to-LDS loads two steps ahead (three
+//   record buffers): raw bytes cost about half the LDS write bandwidth of
 //   dequantized fp16, and LDS writes run at about half the rate of LDS reads
 //   on this GPU.
 // * Each wave dequantizes its own columns once per step, from its records
@@ -42,14 +42,19 @@ constexpr int NS = 4;                        // LDS stages of the X tile
 constexpr int kXStageBytes = BM * BK * 2;    // 16 KB
 constexpr int kXInstr = kXStageBytes / 1024;  // buffer-to-LDS loads per stage (1 KB each)
 // Raw W: each wave owns 32 rows of the tile. A step is 68 bytes of a row,
-// fetched as five 16-byte pieces at byte 0, 16, 32, 48 and 52 (the last two
-// overlap, so nothing past the row's step is read) and kept in the wave's
-// own LDS area as an 80-byte record per row, two steps deep.
+// fetched as five 16-byte pieces at byte 0, 16, 32, 36 and 52 (pieces 2
+// and 3 overlap, so nothing past the row's step is read and block 1's codes
+// are exactly pieces 3 and 4): piece p of the wave's
+// 160 goes to byte 16 p of the step's record buffer, i.e. an 80-byte record
+// per row. Buffer-to-LDS load i writes 64 consecutive pieces, so a record
+// buffer spans kWLoads KB (the last load's spare lanes write its padding).
 constexpr int kWRows = 32;                   // weight rows per wave
 constexpr int kWRec = 80;                    // LDS bytes per row record
 constexpr int kWPieces = 5;
 constexpr int kWLoads = (kWRows * kWPieces + 63) / 64;  // 16-byte loads per lane per step
-constexpr int kWWaveBytes = 2 * kWRows * kWRec;         // per wave, two steps
+constexpr int kWBufs = 3;                              // record buffers per wave
+constexpr int kWBufBytes = kWLoads * 1024;
+constexpr int kWWaveBytes = kWBufs * kWBufBytes;
 
 template <int NWAVES>
 struct Tile {
@@ -59,7 +64,7 @@ struct Tile {
   // stage's kXInstr, so the first kXInstr % NWAVES waves issue one more.
   static constexpr int kXMax = (kXInstr + NWAVES - 1) / NWAVES;
   static constexpr int kLdsBytes = NS * kXStageBytes + NWAVES * kWWaveBytes;
-  static_assert(NS >= 3 && (NS - 2) * (kXMax + kWLoads) <= 63, "vmcnt range");
+  static_assert(NS == 4 && 2 * kXMax + kWLoads <= 63, "pipeline depths and vmcnt range");
 };
 
 // Slot of 16-byte chunk c (0..7) of X tile row r: chunks permuted per row
@@ -136,14 +141,13 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
   // W: piece p = 64 i + lane of this wave's kWRows * 5 pieces (lanes past the
   // last piece repeat it): row p / 5, piece p % 5, kept at byte 16 p of the
   // wave's record area (80 bytes a row).
-  uint32_t woff[kWLoads], wdst[kWLoads];
+  uint32_t woff[kWLoads];
 #pragma unroll
   for (int i = 0; i < kWLoads; ++i) {
     int p = 64 * i + lane;
     p = p < kWRows * kWPieces ? p : kWRows * kWPieces - 1;
     const int rr = p / kWPieces, k = p % kWPieces;
-    woff[i] = (uint32_t)(wave * kWRows + rr) * row_bytes + (k < 4 ? 16 * k : 52);
-    wdst[i] = 16 * p;
+    woff[i] = (uint32_t)(wave * kWRows + rr) * row_bytes + (k < 3 ? 16 * k : k == 3 ? 36 : 52);
   }
   uint8_t *const wl = smem + NS * kXStageBytes + wave * kWWaveBytes;  // this wave's W records
 
@@ -158,33 +162,31 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (wave + i * NWAVES) * 1024, 16,
                                                  (int)xoff[i], ks * (BK * 2), 0, 0);
   };
-  auto load_w = [&](u32x4 (&rw)[kWLoads], int kt) {
+  // This wave's W pieces of step kt into record buffer kt % kWBufs.
+  auto issue_w = [&](int kt) {
     const int ks = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i)
-      rw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)woff[i],
-                                                                              ks * 68, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wl + (kt % kWBufs) * kWBufBytes + i * 1024, 16,
+                                               (int)woff[i], ks * 68, 0, 0);
   };
-  auto store_w = [&](const u32x4 (&rw)[kWLoads], int buf) {
-#pragma unroll
-    for (int i = 0; i < kWLoads; ++i)
-      *reinterpret_cast<u32x4 *>(wl + buf * (kWRows * kWRec) + wdst[i]) = rw[i];
-  };
-
   // B operands of one step from this wave's W records: this lane's column
   // (row l % 32 of the wave) and block h; slice s uses codes 8s .. 8s+7.
-  // Record layout: bytes 0..63 of the step at 0..63, bytes 52..67 at
-  // 64..79, so byte b >= 64 sits at b + 12. Block 0: d and codes in dwords
-  // 0..8 (codes 2 bytes in); block 1: d in the high half of dword 8, codes
-  // in dwords 9..15 and 19 (aligned).
+  // Record pieces: 0 = step bytes 0..15, 1 = 16..31, 2 = 32..47, 3 = 36..51,
+  // 4 = 52..67. The lane reads three whole pieces with 16-byte LDS reads
+  // (the 80-byte record stride keeps eight consecutive lanes on distinct
+  // banks; 4-byte reads at that stride conflicted about 4-way): block 0
+  // takes pieces 0, 1, 2 (d in the low half of dword 0, codes from byte 2),
+  // block 1 takes pieces 3, 4, 2 (codes from byte 0, d in the high half of
+  // the third piece's first dword), so code dword j is alignbyte(D[j + 1],
+  // D[j], 2 - 2h) in both halves.
   auto dequant_step = [&](int buf, half8_t (&b)[4]) {
-    const uint32_t *rw = reinterpret_cast<const uint32_t *>(wl + buf * (kWRows * kWRec) + l32 * kWRec);
-    const uint32_t dword = rw[8 * h];
-    uint32_t q[9];
-#pragma unroll
-    for (int i = 0; i < 7; ++i) q[i] = rw[9 * h + i];
-    q[7] = rw[7 + 12 * h];
-    q[8] = rw[8 + 11 * h];  // unused for block 1 (offset 0)
+    const uint8_t *rec = wl + buf * kWBufBytes + l32 * kWRec;
+    const u32x4 r0 = *reinterpret_cast<const u32x4 *>(rec + 48 * h);
+    const u32x4 r1 = *reinterpret_cast<const u32x4 *>(rec + 16 + 48 * h);
+    const u32x4 r2 = *reinterpret_cast<const u32x4 *>(rec + 32);
+    const uint32_t q[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, r2.x};
+    const uint32_t dword = h ? r2.x : r0.x;
     const half_t dh = __builtin_bit_cast(half_t, (uint16_t)__builtin_amdgcn_ubfe(dword, 16 * h, 16));
     const half2_t d2 = {dh, dh};
     const uint32_t shift = 2 - 2 * h;
@@ -209,38 +211,29 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
-  // Pipeline. X: buffer-to-LDS loads NS - 1 steps ahead, shared by the
-  // workgroup (one barrier per step). W: each wave's own rows, loaded into
-  // registers three steps ahead (two register sets) and written to the
-  // wave's record buffer one step ahead (only this wave reads it, and one
-  // wave's LDS operations complete in order, so no barrier is needed).
-  // Vector-memory loads complete in issue order, so waiting for a register
-  // load also waits for every older load; the register set consumed in step
-  // kt was loaded two iterations earlier, so that this wait leaves the X
-  // loads of the last two iterations in flight. Each iteration issues its W
-  // loads, then its X loads: when step kt's X stage is read, the loads
-  // issued after it are those of the NS - 2 later iterations; the prologue
-  // waits for all of its own loads.
-  u32x4 rw0[kWLoads], rw1[kWLoads];  // W of odd steps in rw1, even steps in rw0
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue_x(s);
-  load_w(rw0, 0);
-  store_w(rw0, 0);
-  load_w(rw1, 1);
-  load_w(rw0, 2);
-  // Step kt: `cur` holds W of step kt + 1 and is refilled with step kt + 3.
-  auto step = [&](int kt, u32x4 (&cur)[kWLoads]) {
+  // Pipeline (all loads are buffer-to-LDS). Iteration kt issues W of step
+  // kt + 2, then X of step kt + 3 (NS - 1 ahead; shared by the workgroup,
+  // one barrier per step). W records are wave-private: only this wave reads
+  // them, so they need no barrier, and the record buffer refilled in step
+  // kt was last read (into registers) in step kt - 1. Loads complete in issue
+  // order; when step kt starts, the loads issued after its W are X of step
+  // kt + 1 and W and X of step kt + 1's iteration, and X of step kt was
+  // issued before its W. The prologue issues in the same order.
+  issue_x(0);
+  issue_w(0);
+  issue_x(1);
+  issue_w(1);
+  issue_x(2);
+  for (int kt = 0; kt < nk; ++kt) {
     if (kXInstr % NWAVES == 0 || nx == kXMax)
-      wait_and_barrier<(NS - 2) * (kXMax + kWLoads)>();
+      wait_and_barrier<2 * kXMax + kWLoads>();
     else
-      wait_and_barrier<(NS - 2) * (kXMax - 1 + kWLoads)>();
-    store_w(cur, (kt + 1) & 1);
-    load_w(cur, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);  // keep the W loads ahead of the X loads
+      wait_and_barrier<2 * (kXMax - 1) + kWLoads>();
+    issue_w(kt + 2);
     issue_x(kt + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
     half8_t b[4];
-    dequant_step(kt & 1, b);
+    dequant_step(kt % kWBufs, b);
     const uint8_t *st = smem + (kt % NS) * kXStageBytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -254,13 +247,7 @@ gemm_q8_0_kernel(const uint8_t *__restrict__ W, const uint16_t *__restrict__ X,
       for (int i = 0; i < 4; ++i)
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[s], acc[i], 0, 0, 0);
     }
-  };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, rw1);
-    step(kt + 1, rw0);
   }
-  if (kt < nk) step(kt, rw1);
   // Drain the loads issued past the end before the workgroup exits.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -506,6 +493,7 @@ int env_waves_override() {
 
 hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,
                             int64_t N, int64_t K, int num_cus, hipStream_t stream) {
+  (void)num_cus;
   if (K % 64 != 0) {
     const int64_t tiles_m = (M + k32::BM - 1) / k32::BM, tiles_n = (N + k32::BN - 1) / k32::BN;
     const int64_t tiles = tiles_m * tiles_n;
@@ -515,18 +503,12 @@ hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, in
                        stream, W, X, Y, M, N, K, (int)tiles_n);
     return hipGetLastError();
   }
-  // Eight waves (128 x 256 tiles), or seven (128 x 224) when that takes
-  // fewer waves' worth of work per CU, counting a partly filled last pass of
-  // tiles over the CUs as a whole one (512 x 14336: 224 tiles of 256
-  // columns leave 32 CUs idle, 256 tiles of 224 columns fill all of them).
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t cus = num_cus > 0 ? num_cus : 1;
-  auto cost = [&](int64_t bn, int64_t waves) {
-    const int64_t t = tiles_m * ((N + bn - 1) / bn);
-    return (t + cus - 1) / cus * waves;
-  };
-  const int env_w = env_waves_override();
-  const bool seven = env_w == 7 || (env_w != 8 && cost(Tile<7>::BN, 7) < cost(Tile<8>::BN, 8));
+  // Eight waves (128 x 256 tiles). Seven (128 x 224) fill more CUs at some
+  // shapes (512 x 14336: 256 tiles instead of 224), but a seven-wave tile
+  // takes as long as an eight-wave one (three of its SIMDs still run two
+  // waves) and measured slower there; it stays available as a tuning
+  // override (LQMM_TUNE_GEMM_WAVES = 7).
+  const bool seven = env_waves_override() == 7;
   return seven ? launch_fast<7>(W, X, Y, M, N, K, stream) : launch_fast<8>(W, X, Y, M, N, K, stream);
 }
 
