@@ -387,12 +387,13 @@ __device__ __forceinline__ u32x4 pack_xword(const XWord &w, float hi_scale) {
 }
 
 // Staged words are grouped by word index t: word t of every (row, unit) pair
-// lies in a block of `stride` slots. The stride is padded to 16/T modulo 16
-// slots (T words per unit), so that the T lanes that stage the words of one
-// (row, unit) pair write to distinct LDS banks.
+// lies in a block of `stride` slots. LDS has 32 banks (8 slots of 16 bytes),
+// and the stride is padded to 8/T modulo 8 slots (T words per unit), so that
+// the eight lanes that stage the words of one or two (row, unit) pairs write
+// to distinct banks.
 template <class F>
 __host__ __device__ __forceinline__ int staged_stride(int n) {
-  return ((n + 15) & ~15) + 16 / F::kWords;
+  return ((n + 7) & ~7) + 8 / F::kWords;
 }
 
 // Stage the words of batch rows 0..nb-1 and units 0..nu-1 into xs, word
