@@ -61,8 +61,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   lqmm_status st = current_device(&num_cus);
   if (st != LQMM_OK) return st;
 
-  const int uw = lqmm::gemv_unit_weights(fmt);
-  const int64_t units_total = K / uw;
+  const int64_t units_total = K / lqmm::gemv_unit_weights(fmt);
   const int64_t row_bytes = K / blk * blk_bytes;
   const int threads = lqmm::gemv_threads();
   const int waves_per_wg = threads / 64;
@@ -75,6 +74,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   const int env_waves = env_int("LQMM_TUNE_GEMV_WAVES");
   const int env_ldsk = env_int("LQMM_TUNE_GEMV_LDSK");
   const int env_depth = env_int("LQMM_TUNE_GEMV_DEPTH");
+  const int env_pair = env_int("LQMM_TUNE_GEMV_Q4_0_PAIR");
 
   for (int64_t b0 = 0; b0 < batch; ) {
     const int64_t left = batch - b0;
@@ -84,6 +84,16 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     if (env_mfma == 0 || env_mfma == 1) mfma = env_mfma == 1;
     const int bmax = mfma ? 16 : 2;
     const int B = (int)(left < bmax ? left : bmax);
+    // VALU-mode Q4_0 takes two blocks per unit when K % 64 == 0: 36-byte,
+    // 4-byte-aligned loads instead of an 18-byte block per lane. Measured:
+    // faster when there are more rows than one workgroup per CU covers (a
+    // wave per two rows), slower with only one workgroup per CU.
+    const int64_t rows_one_wg_per_cu = (int64_t)num_cus * waves_per_wg * 2;
+    bool pair = fmt == GemvFormat::Q4_0 && !mfma && K % 64 == 0 && N > rows_one_wg_per_cu;
+    if (env_pair == 0 || env_pair == 1) pair = fmt == GemvFormat::Q4_0 && !mfma && K % 64 == 0 && env_pair == 1;
+    const GemvFormat f = pair ? GemvFormat::Q4_0x2 : fmt;
+    const int uw = lqmm::gemv_unit_weights(f);
+    const int64_t units = K / uw;
     // MFMA mode uses the coalesced kernel (loads staged through LDS, 8
     // waves) when rows are whole 256-weight super-chunks of 144 bytes and a
     // 16-row tile spans less than 2 GiB (32-bit load offsets); otherwise, or
@@ -116,18 +126,18 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     const int64_t lds_cap = lds_stage ? lqmm::kMaxLds : lqmm::kMaxGemvLds;
     // per-unit cost taken over many units, where the row padding is negligible
     int64_t max_units =
-        (lds_cap - red_bytes) * 4096 / (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, 4096);
+        (lds_cap - red_bytes) * 4096 / (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, 4096);
     // K-split launches start on whole Q4_K super-blocks, and on whole
     // super-chunks for the coalesced kernel.
     const int64_t ustep = lds_stage ? sc_units : fmt == GemvFormat::Q4_K ? 4 : 1;
     max_units -= max_units % ustep;
     // the staged rows are padded: step back until they fit
     while (max_units > ustep &&
-           (int64_t)lqmm::gemv_lds_bytes(fmt, mfma, B, (int)max_units) + red_bytes > lds_cap)
+           (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, (int)max_units) + red_bytes > lds_cap)
       max_units -= ustep;
     if (max_units < ustep) return LQMM_ERR_SHAPE;
-    for (int64_t u0 = 0; u0 < units_total; u0 += max_units) {
-      const int64_t nu64 = units_total - u0 < max_units ? units_total - u0 : max_units;
+    for (int64_t u0 = 0; u0 < units; u0 += max_units) {
+      const int64_t nu64 = units - u0 < max_units ? units - u0 : max_units;
       const int nu = (int)nu64;
       lqmm::GemvPlan pl;
       pl.mfma = mfma;
@@ -135,7 +145,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       int lpr_log2 = 0;
       while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
       pl.lpr_log2 = lpr_log2;
-      pl.lds_bytes = lqmm::gemv_lds_bytes(fmt, mfma, B, nu) + red_bytes;
+      pl.lds_bytes = lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
       int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
       // The coalesced kernel runs one workgroup per CU: each workgroup stages
       // all of x, so more workgroups mostly add staging traffic.
@@ -214,7 +224,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       pl.grid = (int)grid;
       pl.accumulate = u0 > 0;
       const uint8_t *Wb = static_cast<const uint8_t *>(W);
-      hipError_t e = lqmm::gemv_launch(fmt, pl, Wb, x + b0 * K + u0 * uw, y + b0 * N, stream);
+      hipError_t e = lqmm::gemv_launch(f, pl, Wb, x + b0 * K + u0 * uw, y + b0 * N, stream);
       if (e != hipSuccess) return LQMM_ERR_LAUNCH;
     }
     b0 += B;

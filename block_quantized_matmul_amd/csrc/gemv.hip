@@ -96,6 +96,10 @@ struct FmtQ4_0 {
   static constexpr int kUnitWeights = 32;
   static constexpr int kWords = 4;
   static constexpr int kSums = 1;
+  static constexpr int kSumWords = 4;  // words per staged activation sum
+  // Activations of word t: lo values at x_lo(t) .. +3, hi values 16 later.
+  static __device__ __forceinline__ int x_lo(int t) { return 4 * t; }
+  static __device__ __forceinline__ int x_hi(int t) { return 16 + 4 * t; }
   struct Raw {
     u32x4 q;
     uint32_t d;
@@ -123,7 +127,8 @@ struct FmtQ4_0 {
   // VALU mode. Staged sum per (unit, batch row): -(1032*S_lo + 1152*S_hi) with
   // S_lo the sum of the staged lo values and S_hi of the staged x/16 hi
   // values, so that sum_j (q_j - 8) x_j = staged + the dot products.
-  static __device__ __forceinline__ void stage_sums(float *sums, int idx, float slo, float shi) {
+  static __device__ __forceinline__ void stage_sums(float *sums, int idx, int /*g*/, float slo,
+                                                    float shi) {
     sums[idx] = -(1032.0f * slo + 1152.0f * shi);
   }
   // u must index a staged unit; `valid` = 0 makes the unit contribute 0.
@@ -201,6 +206,11 @@ struct FmtQ4_K {
   static constexpr int kUnitWeights = 64;
   static constexpr int kWords = 8;
   static constexpr int kSums = 2;
+  static constexpr int kSumWords = 8;
+  // Activations of word t: sub-block 2i at x_lo(t) .. +3, sub-block 2i + 1
+  // 32 later.
+  static __device__ __forceinline__ int x_lo(int t) { return 4 * t; }
+  static __device__ __forceinline__ int x_hi(int t) { return 32 + 4 * t; }
   struct Raw {
     u32x4 h;   // d | dmin << 16, scales[0..3], scales[4..7], scales[8..11]
     u32x4 q0;  // qs words 0..3 of the pair
@@ -247,7 +257,8 @@ struct FmtQ4_K {
   // VALU mode. Staged sums per (unit, batch row): (-1024*S_lo, -1024*S_hi),
   // which remove the 1024 bias of each dot product and give the activation
   // sums the dmin * m term needs.
-  static __device__ __forceinline__ void stage_sums(float *sums, int idx, float slo, float shi) {
+  static __device__ __forceinline__ void stage_sums(float *sums, int idx, int /*g*/, float slo,
+                                                    float shi) {
     sums[2 * idx] = -1024.0f * slo;
     sums[2 * idx + 1] = -1024.0f * shi;
   }
@@ -362,6 +373,95 @@ struct FmtQ4_K {
   }
 };
 
+// ---- Q4_0 in VALU mode: unit = two consecutive blocks ----------------------
+// 64 weights in 36 bytes at byte 36 u of the row: 4-byte aligned, loaded as
+// 16 + 16 + 4 bytes. A lane that takes one 18-byte block per load issues a
+// 2-byte-aligned 16-byte load and a 2-byte load per block; that pattern
+// streamed at about 3.3 TB/s where aligned 16-byte loads (and this one) reach
+// 4.5 TB/s (27 MiB, cold). Words 0..3 are block 0's qs (2 bytes into the
+// unit, realigned with v_alignbyte_b32), words 4..7 block 1's (aligned).
+// Each block keeps its own scale and its own staged activation sum.
+struct FmtQ4_0x2 {
+  static constexpr int kUnitWeights = 64;
+  static constexpr int kWords = 8;
+  static constexpr int kSums = 2;
+  static constexpr int kSumWords = 4;
+  static __device__ __forceinline__ int x_lo(int t) { return 32 * (t >> 2) + 4 * (t & 3); }
+  static __device__ __forceinline__ int x_hi(int t) { return 16 + x_lo(t); }
+  struct Raw {
+    u32x4 a, b;  // bytes 0..15, 16..31
+    uint32_t c;  // bytes 32..35
+  };
+  static __host__ __device__ __forceinline__ int64_t unit_offset(int64_t unit) { return unit * 36; }
+  static __device__ __forceinline__ Raw load(const uint8_t *row, uint32_t unit) {
+    const uint8_t *p = row + unit * 36u;
+    Raw r;
+    r.a = load_u32x4_unaligned(p);
+    r.b = load_u32x4_unaligned(p + 16);
+    __builtin_memcpy(&r.c, p + 32, 4);
+    return r;
+  }
+  static __device__ __forceinline__ uint32_t word(const Raw &r, int t) {
+    switch (t) {
+      case 0: return __builtin_amdgcn_alignbyte(r.a.y, r.a.x, 2);
+      case 1: return __builtin_amdgcn_alignbyte(r.a.z, r.a.y, 2);
+      case 2: return __builtin_amdgcn_alignbyte(r.a.w, r.a.z, 2);
+      case 3: return __builtin_amdgcn_alignbyte(r.b.x, r.a.w, 2);
+      case 4: return r.b.y;
+      case 5: return r.b.z;
+      case 6: return r.b.w;
+      default: return r.c;
+    }
+  }
+  // Staged sum per (unit, batch row, block g): as for one Q4_0 block.
+  static __device__ __forceinline__ void stage_sums(float *sums, int idx, int g, float slo,
+                                                    float shi) {
+    sums[2 * idx + g] = -(1032.0f * slo + 1152.0f * shi);
+  }
+  template <int B, int R>
+  static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
+                                                 const float *sums, int u, int nu, bool valid,
+                                                 const UnpackMasks &k, float (&acc)[R][B]) {
+    float s[R][B][2];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float c0 = sums[2 * (b * nu + u)], c1 = sums[2 * (b * nu + u) + 1];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        s[r][b][0] = c0;
+        s[r][b][1] = c1;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kWords; ++t) {
+      u32x4 X[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * xstride + u];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        Nibbles n = unpack_word(word(raw[r], t), k);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float a = s[r][b][t >> 2];
+          a = dot2(n.p0, as_half2(X[b].x), a);
+          a = dot2(n.p1, as_half2(X[b].y), a);
+          a = dot2(n.p2, as_half2(X[b].z), a);
+          a = dot2(n.p3, as_half2(X[b].w), a);
+          s[r][b][t >> 2] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float d0 = valid ? f16_bits_to_f32(raw[r].a.x) : 0.0f;
+      const float d1 = valid ? f16_bits_to_f32(raw[r].b.x >> 16) : 0.0f;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        acc[r][b] = __builtin_fmaf(d1, s[r][b][1], __builtin_fmaf(d0, s[r][b][0], acc[r][b]));
+    }
+  }
+};
+
 // ---- activation staging ------------------------------------------------------
 // Word (b, u, t) holds the 8 activations of word t of unit u for batch row b,
 // in unpack order; `hi_scale` multiplies the hi values (1/16 in VALU mode so
@@ -372,9 +472,9 @@ struct XWord {
 template <class F>
 __device__ __forceinline__ XWord load_xword(const float *__restrict__ x, int64_t ldx, int b, int u,
                                             int t) {
-  const float *base = x + b * ldx + (int64_t)u * F::kUnitWeights + 4 * t;
-  return XWord{*reinterpret_cast<const float4_t *>(base),
-               *reinterpret_cast<const float4_t *>(base + F::kUnitWeights / 2)};
+  const float *base = x + b * ldx + (int64_t)u * F::kUnitWeights;
+  return XWord{*reinterpret_cast<const float4_t *>(base + F::x_lo(t)),
+               *reinterpret_cast<const float4_t *>(base + F::x_hi(t))};
 }
 __device__ __forceinline__ u32x4 pack_xword(const XWord &w, float hi_scale) {
   const float4_t hi = w.hi * hi_scale;
@@ -494,10 +594,14 @@ gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int
   __syncthreads();
   for (int i = tid; i < B * nu; i += kGemvThreads) {
     const int u = i % nu, b = i / nu;
-    float slo = 0.0f, shi = 0.0f;
 #pragma unroll
-    for (int t = 0; t < T; ++t) word_sums(xs[(b * T + t) * NS + u], slo, shi);
-    F::stage_sums(sums, i, slo, shi);
+    for (int g = 0; g < T / F::kSumWords; ++g) {
+      float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+      for (int t = g * F::kSumWords; t < (g + 1) * F::kSumWords; ++t)
+        word_sums(xs[(b * T + t) * NS + u], slo, shi);
+      F::stage_sums(sums, i, g, slo, shi);
+    }
   }
   __syncthreads();
 
@@ -1069,35 +1173,44 @@ hipError_t launch_ru(const GemvPlan &pl, const uint8_t *W, const float *x, float
   return launch_valu<F, B, 2, 2, FULL>(pl, W, x, y, s);
 }
 
+// Matrix-core launches (Q4_0 and Q4_K).
+template <class F>
+hipError_t launch_fmt_mfma(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                           hipStream_t s) {
+  const int u = pl.units_per_lane;
+  if (pl.lds_stage) {
+    if (std::is_same<F, FmtQ4_K>::value) return launch_coal_fmt<CoalQ4_K>(pl, W, x, y, s);
+    return launch_coal_fmt<CoalQ4_0>(pl, W, x, y, s);
+  }
+  if (pl.waves == 16) {
+    switch (pl.ksplit) {
+      case 4: return u == 4 ? launch_mfma<F, 1, 4, 4, 16>(pl, W, x, y, s)
+                            : launch_mfma<F, 1, 2, 4, 16>(pl, W, x, y, s);
+      case 8: return u == 4 ? launch_mfma<F, 1, 4, 8, 16>(pl, W, x, y, s)
+                            : launch_mfma<F, 1, 2, 8, 16>(pl, W, x, y, s);
+      default: return u == 4 ? launch_mfma<F, 1, 4, 16, 16>(pl, W, x, y, s)
+                             : launch_mfma<F, 1, 2, 16, 16>(pl, W, x, y, s);
+    }
+  }
+  switch (pl.ksplit) {
+    case 1: return u == 4 ? launch_mfma<F, 1, 4, 1, 8>(pl, W, x, y, s)
+                          : launch_mfma<F, 1, 2, 1, 8>(pl, W, x, y, s);
+    case 2: return u == 4 ? launch_mfma<F, 1, 4, 2, 8>(pl, W, x, y, s)
+                          : launch_mfma<F, 1, 2, 2, 8>(pl, W, x, y, s);
+    case 4: return u == 4 ? launch_mfma<F, 1, 4, 4, 8>(pl, W, x, y, s)
+                          : launch_mfma<F, 1, 2, 4, 8>(pl, W, x, y, s);
+    default: return u == 4 ? launch_mfma<F, 1, 4, 8, 8>(pl, W, x, y, s)
+                           : launch_mfma<F, 1, 2, 8, 8>(pl, W, x, y, s);
+  }
+}
+
 template <class F>
 hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                       hipStream_t s) {
-  if (pl.mfma) {
-    const int u = pl.units_per_lane;
-    if (pl.lds_stage) {
-      if (std::is_same<F, FmtQ4_K>::value) return launch_coal_fmt<CoalQ4_K>(pl, W, x, y, s);
-      return launch_coal_fmt<CoalQ4_0>(pl, W, x, y, s);
-    }
-    if (pl.waves == 16) {
-      switch (pl.ksplit) {
-        case 4: return u == 4 ? launch_mfma<F, 1, 4, 4, 16>(pl, W, x, y, s)
-                              : launch_mfma<F, 1, 2, 4, 16>(pl, W, x, y, s);
-        case 8: return u == 4 ? launch_mfma<F, 1, 4, 8, 16>(pl, W, x, y, s)
-                              : launch_mfma<F, 1, 2, 8, 16>(pl, W, x, y, s);
-        default: return u == 4 ? launch_mfma<F, 1, 4, 16, 16>(pl, W, x, y, s)
-                               : launch_mfma<F, 1, 2, 16, 16>(pl, W, x, y, s);
-      }
-    }
-    switch (pl.ksplit) {
-      case 1: return u == 4 ? launch_mfma<F, 1, 4, 1, 8>(pl, W, x, y, s)
-                            : launch_mfma<F, 1, 2, 1, 8>(pl, W, x, y, s);
-      case 2: return u == 4 ? launch_mfma<F, 1, 4, 2, 8>(pl, W, x, y, s)
-                            : launch_mfma<F, 1, 2, 2, 8>(pl, W, x, y, s);
-      case 4: return u == 4 ? launch_mfma<F, 1, 4, 4, 8>(pl, W, x, y, s)
-                            : launch_mfma<F, 1, 2, 4, 8>(pl, W, x, y, s);
-      default: return u == 4 ? launch_mfma<F, 1, 4, 8, 8>(pl, W, x, y, s)
-                             : launch_mfma<F, 1, 2, 8, 8>(pl, W, x, y, s);
-    }
+  if constexpr (std::is_same<F, FmtQ4_0x2>::value) {  // VALU mode only
+    if (pl.mfma || pl.lds_stage) return hipErrorInvalidValue;
+  } else {
+    if (pl.mfma) return launch_fmt_mfma<F>(pl, W, x, y, s);
   }
   const bool full = pl.lpr_log2 == 6;
   if (pl.batch == 1)
@@ -1114,8 +1227,11 @@ size_t staged_bytes(bool mfma, int batch, int nu) {
 }
 
 size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu) {
-  return f == GemvFormat::Q4_0 ? staged_bytes<FmtQ4_0>(mfma, batch, nu)
-                               : staged_bytes<FmtQ4_K>(mfma, batch, nu);
+  switch (f) {
+    case GemvFormat::Q4_0: return staged_bytes<FmtQ4_0>(mfma, batch, nu);
+    case GemvFormat::Q4_0x2: return staged_bytes<FmtQ4_0x2>(mfma, batch, nu);
+    default: return staged_bytes<FmtQ4_K>(mfma, batch, nu);
+  }
 }
 
 size_t gemv_mfma_reduce_bytes(int waves) { return (size_t)waves * kWave * 16; }
@@ -1125,7 +1241,9 @@ size_t gemv_coal_stage_bytes(int u) {
 }
 
 int gemv_unit_weights(GemvFormat f) {
-  return f == GemvFormat::Q4_0 ? FmtQ4_0::kUnitWeights : FmtQ4_K::kUnitWeights;
+  return f == GemvFormat::Q4_0 ? FmtQ4_0::kUnitWeights
+         : f == GemvFormat::Q4_0x2 ? FmtQ4_0x2::kUnitWeights
+                                   : FmtQ4_K::kUnitWeights;
 }
 
 int gemv_threads() { return kGemvThreads; }
@@ -1133,6 +1251,7 @@ int gemv_threads() { return kGemvThreads; }
 hipError_t gemv_launch(GemvFormat f, const GemvPlan &pl, const uint8_t *W, const float *x,
                        float *y, hipStream_t stream) {
   if (f == GemvFormat::Q4_0) return launch_fmt<FmtQ4_0>(pl, W, x, y, stream);
+  if (f == GemvFormat::Q4_0x2) return launch_fmt<FmtQ4_0x2>(pl, W, x, y, stream);
   return launch_fmt<FmtQ4_K>(pl, W, x, y, stream);
 }
 

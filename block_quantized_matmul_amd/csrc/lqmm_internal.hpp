@@ -9,7 +9,9 @@
 namespace lqmm {
 
 // ---- GEMV -------------------------------------------------------------------
-enum class GemvFormat { Q4_0, Q4_K };
+// Q4_0x2: Q4_0 weights taken two blocks (64 weights, 36 bytes) per unit, used
+// by the VALU-mode kernel when K % 64 == 0.
+enum class GemvFormat { Q4_0, Q4_K, Q4_0x2 };
 
 // Largest dynamic LDS one GEMV launch may use (staged activations + sums).
 constexpr int kMaxGemvLds = 144 * 1024;

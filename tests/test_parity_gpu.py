@@ -57,6 +57,22 @@ def test_q4_0_small(orc, N, K, B):
     assert_close(y, ref, TOL_QUANT, f"q4_0 {N}x{K} b{B}")
 
 
+@pytest.mark.parametrize("pair", [0, 1])
+@pytest.mark.parametrize("N,K,B", [(1, 64, 1), (7, 128, 2), (13, 96, 1), (33, 4096, 1),
+                                   (1000, 512, 1), (64, 1024, 2), (2, 160, 2),
+                                   # K split over launches that accumulate into y
+                                   (5, 73728, 1), (5, 73728, 2), (3, 73760, 1)])
+def test_q4_0_dot2_units(orc, monkeypatch, pair, N, K, B):
+    # the dot2 path (batch <= 2) with one block per unit and with two (taken
+    # only when K % 64 == 0), forced through the planner's tuning override
+    monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", str(pair))
+    c = synth.q4_0_case(N, K, B, seed=N * 5 + K + B + pair)
+    announce(f"q4_0 gemv N={N} K={K} batch={B} pair={pair}")
+    y = _run_q4_0(c)
+    ref = orc.gemv_q4_0(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"q4_0 {N}x{K} b{B} pair={pair}")
+
+
 @pytest.mark.parametrize("name", ["q4_0_gemv_1024", "q4_0_gemv_4096x4096_b1",
                                   "q4_0_gemv_4096x4096_b4", "q4_0_gemv_11008x4096_b1",
                                   "q4_0_gemv_11008x4096_b4", "q4_0_gemv_12288x4096_b1",
@@ -69,11 +85,14 @@ def test_q4_0_configs(orc, name):
     assert_close(y, ref, TOL_QUANT, name)
 
 
-def test_q4_0_one_hot_exact(orc):
-    """One-hot activations extract weight columns. dot2 path (batch <= 2):
-    bit-exact (x = 1 is exact in fp16 and every partial sum is an exact small
-    integer). Matrix-core path (batch >= 3): the weight is rounded once to
-    fp16, so the result is exactly the fp16-rounded column."""
+@pytest.mark.parametrize("pair", [0, 1])
+def test_q4_0_one_hot_exact(orc, monkeypatch, pair):
+    """One-hot activations extract weight columns. dot2 path (batch <= 2),
+    with one or two blocks per unit: bit-exact (x = 1 is exact in fp16 and
+    every partial sum is an exact small integer). Matrix-core path (batch >=
+    3): the weight is rounded once to fp16, so the result is exactly the
+    fp16-rounded column."""
+    monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", str(pair))
     c = synth.make("q4_0_gemv_1024")
     ks = [0, 1, 15, 16, 17, 31, 32, 500, 1007, 1023]
     x = np.zeros((len(ks), c.K), np.float32)
@@ -145,7 +164,9 @@ def test_q4_0_deterministic():
 # ----------------------------------------------------------------- Q4_K GEMV
 Q4_K_SMALL = [(1, 256, 1), (3, 512, 2), (17, 768, 8), (5, 256, 9), (9, 8704, 8),
               (70, 2048, 3), (129, 4096, 5), (2, 1280, 4), (40, 16384, 1), (257, 256, 6),
-              (33, 4608, 16), (18, 2048, 19), (48, 18432, 12)]
+              (33, 4608, 16), (18, 2048, 19), (48, 18432, 12),
+              # dot2 path with K split over three launches
+              (3, 147456, 1)]
 
 
 @pytest.mark.parametrize("N,K,B", Q4_K_SMALL)
