@@ -75,6 +75,37 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   const int env_ldsk = env_int("LQMM_TUNE_GEMV_LDSK");
   const int env_depth = env_int("LQMM_TUNE_GEMV_DEPTH");
   const int env_pair = env_int("LQMM_TUNE_GEMV_Q4_0_PAIR");
+  const int env_xregs = env_int("LQMM_TUNE_GEMV_XREGS");
+  const int64_t tiles = (N + 15) / 16;  // 16-row tiles of the matrix-core kernels
+
+  // K-slices per tile of the coalesced kernel (one workgroup per CU): the
+  // number that gives each wave the fewest units, counting the last, partly
+  // filled pass of workgroups over the CUs as a whole one; ties go to more
+  // slices. With the activations in registers (xr), at most four
+  // super-chunks per slice. Then the tuning override; every slice must hold
+  // a whole chunk of uu super-chunks (uu drops to 1 for rows shorter than a
+  // chunk).
+  auto coal_slices = [&](int64_t nu, int &uu, bool xr, int sc_units) -> int {
+    int ks = 1;
+    int64_t best = -1;
+    for (int k = 8; k >= 1; k /= 2) {
+      if (xr && (nu / sc_units + k - 1) / k > 4) continue;
+      const int64_t wgs = (tiles * k + 7) / 8;
+      const int64_t grid_k = wgs < (int64_t)num_cus ? wgs : (int64_t)num_cus;
+      const int64_t upc = (int64_t)sc_units * uu;  // units per chunk
+      const int64_t slice = ((nu + k - 1) / k + upc - 1) / upc * upc;
+      const int64_t cost = (wgs + grid_k - 1) / grid_k * slice;
+      if (best < 0 || cost < best) {
+        best = cost;
+        ks = k;
+      }
+    }
+    if (env_ks >= 1 && env_ks <= 8 && (env_ks & (env_ks - 1)) == 0) ks = env_ks;
+    while (ks > 1 && (nu / ks) < sc_units * uu) ks /= 2;
+    if (nu < sc_units * uu) uu = 1;
+    while (xr && (nu / sc_units + ks - 1) / ks > 4 && ks < 8) ks *= 2;
+    return ks;
+  };
 
   for (int64_t b0 = 0; b0 < batch; ) {
     const int64_t left = batch - b0;
@@ -101,6 +132,24 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     const int sc_units = fmt == GemvFormat::Q4_K ? 4 : 8;  // units per super-chunk
     const bool lds_stage = mfma && env_ldsk != 0 && units_total % sc_units == 0 &&
                            16 * row_bytes < ((int64_t)1 << 31);
+    // Its variant with the activations in registers takes the whole K in one
+    // launch when k-slices of at most four super-chunks cover a row (up to 32
+    // super-chunks, with eight slices) and a slice's activations fit in one
+    // wave's chunk ring for staging. Measured: faster when every wave
+    // computes at least 12 chunks (Q4_K 28672 x 8192 at 8 rows: 28), slower
+    // below about 6 (its per-wave staging comes before the first chunk
+    // request).
+    bool xregs = lds_stage && env_xregs != 0 && units_total / sc_units <= 32;
+    if (xregs) {
+      int uu1 = 1;
+      const int ks = coal_slices(units, uu1, true, sc_units);
+      const int64_t cps = (units / sc_units + ks - 1) / ks;
+      xregs = lqmm::gemv_coalr_fits(fmt, (int)cps, B);
+      const int64_t wgs = (tiles * ks + 7) / 8;
+      const int64_t grid = wgs < (int64_t)num_cus ? wgs : (int64_t)num_cus;
+      const int64_t tiles_per_wave = (tiles + grid * (8 / ks) - 1) / (grid * (8 / ks));
+      if (env_xregs != 1) xregs = xregs && tiles_per_wave * cps >= 12;
+    }
     // Other MFMA launches: 16-wave workgroups when the staged activations
     // leave room for only one workgroup per CU, so that more loads are in
     // flight.
@@ -112,7 +161,8 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     }
     // One super-chunk per row per chunk, two for large N at up to six
     // activation rows (long K-slices; the staged activations leave room).
-    const int lds_u = lds_stage ? ((env_u == 1 || env_u == 2)
+    const int lds_u = xregs ? 1
+                      : lds_stage ? ((env_u == 1 || env_u == 2)
                                        ? env_u
                                        : (B <= 6 && N > 6 * 16 * (int64_t)num_cus ? 2 : 1))
                                 : 0;
@@ -125,17 +175,19 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
                           : (int64_t)lqmm::gemv_mfma_reduce_bytes(waves);
     const int64_t lds_cap = lds_stage ? lqmm::kMaxLds : lqmm::kMaxGemvLds;
     // per-unit cost taken over many units, where the row padding is negligible
-    int64_t max_units =
-        (lds_cap - red_bytes) * 4096 / (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, 4096);
-    // K-split launches start on whole Q4_K super-blocks, and on whole
-    // super-chunks for the coalesced kernel.
-    const int64_t ustep = lds_stage ? sc_units : fmt == GemvFormat::Q4_K ? 4 : 1;
-    max_units -= max_units % ustep;
-    // the staged rows are padded: step back until they fit
-    while (max_units > ustep &&
-           (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, (int)max_units) + red_bytes > lds_cap)
-      max_units -= ustep;
-    if (max_units < ustep) return LQMM_ERR_SHAPE;
+    int64_t max_units = units;
+    if (!xregs) {
+      max_units = (lds_cap - red_bytes) * 4096 / (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, 4096);
+      // K-split launches start on whole Q4_K super-blocks, and on whole
+      // super-chunks for the coalesced kernel.
+      const int64_t ustep = lds_stage ? sc_units : fmt == GemvFormat::Q4_K ? 4 : 1;
+      max_units -= max_units % ustep;
+      // the staged rows are padded: step back until they fit
+      while (max_units > ustep &&
+             (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, (int)max_units) + red_bytes > lds_cap)
+        max_units -= ustep;
+      if (max_units < ustep) return LQMM_ERR_SHAPE;
+    }
     for (int64_t u0 = 0; u0 < units; u0 += max_units) {
       const int64_t nu64 = units - u0 < max_units ? units - u0 : max_units;
       const int nu = (int)nu64;
@@ -145,7 +197,8 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       int lpr_log2 = 0;
       while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
       pl.lpr_log2 = lpr_log2;
-      pl.lds_bytes = lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
+      pl.lds_bytes = xregs ? lqmm::gemv_coalr_lds_bytes()
+                           : lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
       int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
       // The coalesced kernel runs one workgroup per CU: each workgroup stages
       // all of x, so more workgroups mostly add staging traffic.
@@ -156,41 +209,23 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       if (mfma) {
         // R = 1 tile of 16 rows per team; KS waves share a tile along K so
         // that small N still gives every CU several waves.
-        const int64_t tiles = (N + 15) / 16;
         int uu = lds_stage ? lds_u : 2, ks = waves == 16 ? 4 : 1;
         const int ksmax = waves == 16 ? 16 : 8;
-        while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
-        // Coalesced kernel (one workgroup per CU): the number of K-slices per
-        // tile that gives each wave the fewest units, counting the last,
-        // partly filled pass of workgroups over the CUs as a whole one; ties
-        // go to more slices.
         if (lds_stage) {
-          int64_t best = -1;
-          for (int k = 8; k >= 1; k /= 2) {
-            const int64_t wgs = (tiles * k + 7) / 8;
-            const int64_t grid_k = wgs < (int64_t)num_cus * wg_per_cu ? wgs : (int64_t)num_cus * wg_per_cu;
-            const int64_t upc = (int64_t)sc_units * uu;  // units per chunk
-            const int64_t slice = ((nu + k - 1) / k + upc - 1) / upc * upc;
-            const int64_t cost = (wgs + grid_k - 1) / grid_k * slice;
-            if (best < 0 || cost < best) {
-              best = cost;
-              ks = k;
-            }
-          }
-        }
-        if (!lds_stage && (env_u == 2 || env_u == 4)) uu = env_u;
-        if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
-          ks = env_ks;
-        // every slice must hold a whole chunk of uu super-chunks
-        if (lds_stage) {
-          while (ks > 1 && (nu / ks) < sc_units * uu) ks /= 2;
-          if (nu < sc_units * uu) uu = 1;
+          ks = coal_slices(nu, uu, xregs, sc_units);
+        } else {
+          while (ks < ksmax && tiles * ks < (int64_t)num_cus * 8 && nu >= 2 * ks * 4 * uu) ks *= 2;
+          if (env_u == 2 || env_u == 4) uu = env_u;
+          if (env_ks >= (waves == 16 ? 4 : 1) && env_ks <= ksmax && (env_ks & (env_ks - 1)) == 0)
+            ks = env_ks;
         }
         pl.rows_per_lane = 1;
         pl.units_per_lane = uu;
         pl.ksplit = ks;
         pl.waves = waves;
         pl.lds_stage = lds_stage;
+        pl.xregs = xregs;
+        pl.cps = xregs ? (nu / sc_units + ks - 1) / ks : 0;
         pl.depth = (env_depth == 2 || env_depth == 3 || env_depth == 4 || env_depth == 6) ? env_depth : 2;
         const int teams = waves / ks;
         wg_needed = (tiles + teams - 1) / teams;
@@ -207,6 +242,8 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         pl.ksplit = 1;
         pl.waves = waves_per_wg;
         pl.lds_stage = 0;
+        pl.xregs = 0;
+        pl.cps = 0;
         pl.depth = 2;
         const int64_t groups = (N + (int64_t)slots * r - 1) / ((int64_t)slots * r);
         wg_needed = (groups + waves_per_wg - 1) / waves_per_wg;

@@ -45,6 +45,7 @@ namespace {
 constexpr int kGemvThreads = 512;
 constexpr int kWavesPerWg = kGemvThreads / kWave;
 constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
+constexpr int kCoalrRing = 6;  // chunk slots per wave of gemv_coalr_kernel
 
 // Unpack one 32-bit word of nibbles (bytes e = 0..3, each holding a "lo"
 // nibble and a "hi" nibble) into four fp16 pairs:
@@ -1078,6 +1079,206 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
     if (it + k < n_items) stage(bufs[k]);
 }
 
+// ---- MFMA mode, coalesced loads, activations in registers ---------------------
+// The tiles, k-slices, chunk loads and B-operand layout of gemv_coal_kernel
+// (one super-chunk per chunk), for launches whose k-slice spans at most CPS
+// <= 4 super-chunks. A wave's slice is the same for every tile it visits, so
+// it loads the fp16 A operands of its slice into registers once (32 VGPRs per
+// super-chunk; lanes whose batch row n >= nb hold zeros). LDS then holds only
+// a ring of DR chunk slots per wave, filled by buffer-to-LDS loads DR - 1
+// chunks ahead of the one being computed (no register round trip, no LDS
+// write instructions), and a k-split reduction area that alternates between
+// tiles, so that each tile needs one barrier.
+//
+// Waits: the compiler does not see the LDS data the buffer-to-LDS loads
+// write, so the wave waits for them explicitly. At the top of chunk i the
+// loads of chunks i+1 .. i+DR-1 (NI each) may stay in flight; loads return
+// in order. Stores to y issued after them are not counted, which can only
+// make the wait longer, never too short. A slot is refilled only after the
+// wave's reads of it have completed. Chunks past the end of the wave's work
+// are requested from an empty buffer range: they return zeros, touch no
+// memory, and keep the count of loads in flight constant.
+template <class C, int CPS, int KS, int DR>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
+                  const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int64_t ldy,
+                  int64_t N, int nb, int accumulate) {
+  using F = typename C::F;
+  constexpr int NW = kWavesPerWg;
+  constexpr int T = F::kWords;
+  constexpr int LU = C::kLaneUnits;
+  constexpr int kTeams = NW / KS;
+  constexpr int PR = 9;                // 16-byte pieces of one row's super-chunk
+  constexpr int NP = 16 * PR;          // pieces per chunk
+  constexpr int NI = (NP + 63) / 64;   // loads per lane per chunk
+  constexpr int kSlot = NI * kWave * 16;
+  static_assert((DR - 1) * NI <= 63, "load counter range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int team = wave / KS, slice = wave % KS;
+  const int lane = tid & (kWave - 1);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+  uint8_t *const ring = smem + wave * (DR * kSlot);
+  float4_t *const red = reinterpret_cast<float4_t *>(smem + NW * DR * kSlot);  // [2][NW][kWave]
+  const int ngroups = (int)((N + 15) / 16);
+  const int nsc = nu / C::kUnitsPerSC;  // super-chunks per row in this launch
+  const int sc0 = slice * CPS;          // first super-chunk of this wave's slice
+  const int group_stride = gridDim.x * kTeams;
+  const int gfirst = blockIdx.x * kTeams;
+  // Tiles per wave: the same for every wave of the workgroup (counted from
+  // team 0's first tile), so the reduction barriers match.
+  const int n_tiles = gfirst < ngroups ? (ngroups - gfirst + group_stride - 1) / group_stride : 0;
+  const uint32_t unit0_bytes = (uint32_t)(unit0 / C::kUnitsPerSC * 144);
+
+  uint32_t off[NI];
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int pc = k * kWave + lane;
+    off[k] = pc < NP ? (uint32_t)(pc / PR) * (uint32_t)row_bytes + (uint32_t)(pc % PR) * 16
+                     : 0x80000000u;
+  }
+
+  // Request chunk (item) `it` of this wave into ring slot `slot`: tile
+  // gfirst + team + (it / CPS) * group_stride, super-chunk sc0 + it % CPS
+  // (clamped into the row; such chunks are zeroed at compute time).
+  int ig = gfirst + team, ic = 0, issued = 0;
+  const int n_items = n_tiles * CPS;
+  auto issue = [&](int slot) {
+    const bool live = issued < n_items;
+    const int gc = ig < ngroups ? ig : ngroups - 1;
+    const int64_t r0 = (int64_t)gc * 16;
+    const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+    const rsrc_t rs = make_rsrc(W + r0 * row_bytes + unit0_bytes,
+                                live ? (uint32_t)(rows * row_bytes - unit0_bytes) : 0u);
+    const int sc = sc0 + ic < nsc ? sc0 + ic : nsc - 1;
+#pragma unroll
+    for (int k = 0; k < NI; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring + slot * kSlot + k * (kWave * 16), 16,
+                                               (int)off[k], sc * 144, 0, 0);
+    ++issued;
+    if (++ic == CPS) {
+      ic = 0;
+      ig += group_stride;
+    }
+  };
+  // A operands of the slice (super-chunk c, lane unit j, word t). Loaded in
+  // the A-operand layout straight from memory, every 16-byte load would touch
+  // one cache line per lane; instead the wave stages its slice as fp16 words
+  // in its own ring area with coalesced loads (word (b, u, t) at slot
+  // t * TS + u * nb + b, as the LDS-staged kernels lay it out), reads its
+  // operands back, and only then requests its first chunks into that area.
+  // (Chunks requested earlier into free slots made the staging loads wait
+  // for them: loads return in order.) Units past the row end stage zeros;
+  // lanes n >= nb take zeros.
+  constexpr int nus = CPS * C::kUnitsPerSC;  // units of the slice
+  u32x4 xr[CPS][LU * T];
+  {
+    u32x4 *const xs = reinterpret_cast<u32x4 *>(ring);
+    const int TS = staged_stride<F>(nus * nb);
+    const int ubase = slice * nus;
+    const int total = nb * nus * T;
+    // words in flight per lane: a batch past `total` loads clamped
+    // duplicates, so small slices want small batches (measured: 4 is as
+    // fast as 8 at eight activation rows and faster at four)
+    constexpr int kXB = 4;
+    for (int base = lane; base < total; base += kXB * kWave) {
+      XWord w[kXB];
+      int dst[kXB];
+      bool zero[kXB];
+#pragma unroll
+      for (int k = 0; k < kXB; ++k) {
+        const int i = base + k * kWave;
+        const int ic = i < total ? i : total - 1;
+        const int t = ic % T, r = ic / T;
+        const int b = r % nb, u = r / nb;
+        const int ua = ubase + u < nu ? ubase + u : nu - 1;
+        w[k] = load_xword<F>(x, ldx, b, ua, t);
+        dst[k] = i < total ? t * TS + u * nb + b : -1;
+        zero[k] = ubase + u >= nu;
+      }
+#pragma unroll
+      for (int k = 0; k < kXB; ++k)
+        if (dst[k] >= 0) xs[dst[k]] = zero[k] ? u32x4{0, 0, 0, 0} : pack_xword(w[k], 1.0f);
+    }
+    const int xn = n < nb ? n : 0;
+#pragma unroll
+    for (int c = 0; c < CPS; ++c)
+#pragma unroll
+      for (int j = 0; j < LU; ++j)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const u32x4 v = xs[t * TS + (c * C::kUnitsPerSC + q * LU + j) * nb + xn];
+          xr[c][j * T + t] = n < nb ? v : u32x4{0, 0, 0, 0};
+        }
+    // the chunk requests below overwrite the staged words
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  int slot = 0;  // ring slot of the next item to compute
+#pragma unroll
+  for (int k = 0; k < DR; ++k) issue(k);
+
+  const UnpackMasks kmask;
+  float4_t acc = float4_t{0, 0, 0, 0};
+  int par = 0;
+  int cg = gfirst + team;  // tile being computed
+  for (int tt = 0; tt < n_tiles; ++tt) {
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+      // keep the previous chunk's work ahead of this chunk's wait
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+      const u32x4 *wbuf = reinterpret_cast<const u32x4 *>(ring + slot * kSlot);
+      typename F::Raw rw[LU];
+#pragma unroll
+      for (int j = 0; j < LU; ++j) rw[j] = C::read(wbuf + n * PR, q, j);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(slot);
+      slot = slot + 1 == DR ? 0 : slot + 1;
+      const bool valid = sc0 + c < nsc;
+#pragma unroll
+      for (int j = 0; j < LU; ++j) {
+        const typename F::Prep pr = F::prep(rw[j], q, valid);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const half8_t a = __builtin_bit_cast(half8_t, xr[c][j * T + t]);
+          const half8_t wv = __builtin_bit_cast(half8_t, F::dequant(rw[j], pr, t, kmask));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wv, acc, 0, 0, 0);
+        }
+      }
+    }
+    if (KS > 1) {
+      red[(par * NW + wave) * kWave + lane] = acc;
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (slice == 0) {
+#pragma unroll
+        for (int s2 = 1; s2 < KS; ++s2) acc += red[(par * NW + wave + s2) * kWave + lane];
+      }
+      par ^= 1;
+    }
+    if (slice == 0 && cg < ngroups) {
+      const int64_t row = (int64_t)cg * 16 + n;
+      if (row < N) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int b = 4 * q + v;
+          if (b < nb) {
+            float val = acc[v];
+            if (accumulate) val += y[b * ldy + row];
+            y[b * ldy + row] = val;
+          }
+        }
+      }
+    }
+    acc = float4_t{0, 0, 0, 0};
+    cg += group_stride;
+  }
+  // no buffer-to-LDS load may be left in flight when the wave ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <class K>
 hipError_t set_lds_attr(K kern) {
   return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1146,6 +1347,45 @@ hipError_t launch_coal_fmt(const GemvPlan &pl, const uint8_t *W, const float *x,
   return launch_coal_d<C, 1>(pl, W, x, y, s);
 }
 
+// Activations-in-registers instances: CPS in {1, 2, 3, 4} super-chunks per
+// k-slice, KS in {1, 2, 4, 8}, a ring of kCoalrRing chunks per wave.
+template <class C, int CPS, int KS>
+hipError_t launch_coalr(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                        hipStream_t stream) {
+  auto kern = gemv_coalr_kernel<C, CPS, KS, kCoalrRing>;
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, stream, W,
+                     pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
+                     pl.accumulate);
+  return hipGetLastError();
+}
+template <class C, int CPS>
+hipError_t launch_coalr_ks(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                           hipStream_t s) {
+  switch (pl.ksplit) {
+    case 1: return launch_coalr<C, CPS, 1>(pl, W, x, y, s);
+    case 2: return launch_coalr<C, CPS, 2>(pl, W, x, y, s);
+    case 4: return launch_coalr<C, CPS, 4>(pl, W, x, y, s);
+    default: return launch_coalr<C, CPS, 8>(pl, W, x, y, s);
+  }
+}
+template <class C>
+hipError_t launch_coalr_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                            hipStream_t s) {
+  switch (pl.cps) {
+    case 1: return launch_coalr_ks<C, 1>(pl, W, x, y, s);
+    case 2: return launch_coalr_ks<C, 2>(pl, W, x, y, s);
+    case 3: return launch_coalr_ks<C, 3>(pl, W, x, y, s);
+    default: return launch_coalr_ks<C, 4>(pl, W, x, y, s);
+  }
+}
+
 template <class F, int R, int U, int KS, int NW>
 hipError_t launch_mfma(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                        hipStream_t stream) {
@@ -1179,6 +1419,11 @@ hipError_t launch_fmt_mfma(const GemvPlan &pl, const uint8_t *W, const float *x,
                            hipStream_t s) {
   const int u = pl.units_per_lane;
   if (pl.lds_stage) {
+    if (pl.xregs) {
+      if (pl.cps < 1 || pl.cps > 4) return hipErrorInvalidValue;
+      if (std::is_same<F, FmtQ4_K>::value) return launch_coalr_fmt<CoalQ4_K>(pl, W, x, y, s);
+      return launch_coalr_fmt<CoalQ4_0>(pl, W, x, y, s);
+    }
     if (std::is_same<F, FmtQ4_K>::value) return launch_coal_fmt<CoalQ4_K>(pl, W, x, y, s);
     return launch_coal_fmt<CoalQ4_0>(pl, W, x, y, s);
   }
@@ -1235,6 +1480,18 @@ size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu) {
 }
 
 size_t gemv_mfma_reduce_bytes(int waves) { return (size_t)waves * kWave * 16; }
+
+bool gemv_coalr_fits(GemvFormat f, int cps, int batch) {
+  const int T = f == GemvFormat::Q4_K ? FmtQ4_K::kWords : FmtQ4_0::kWords;
+  const int scu = f == GemvFormat::Q4_K ? CoalQ4_K::kUnitsPerSC : CoalQ4_0::kUnitsPerSC;
+  const int ts = f == GemvFormat::Q4_K ? staged_stride<FmtQ4_K>(cps * scu * batch)
+                                       : staged_stride<FmtQ4_0>(cps * scu * batch);
+  return (size_t)T * ts * 16 <= (size_t)kCoalrRing * 3 * kWave * 16;
+}
+
+size_t gemv_coalr_lds_bytes() {
+  return (size_t)kWavesPerWg * kCoalrRing * 3 * kWave * 16 + (size_t)2 * kWavesPerWg * kWave * 16;
+}
 
 size_t gemv_coal_stage_bytes(int u) {
   return (size_t)kWavesPerWg * ((16 * 9 * u + 63) / 64) * kWave * 16;

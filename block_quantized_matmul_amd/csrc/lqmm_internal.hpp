@@ -25,7 +25,9 @@ struct GemvPlan {
   int waves;          // MFMA mode: waves per workgroup (8 or 16)
   int lds_stage;      // MFMA mode: coalesced loads staged through LDS (8 waves; units_per_lane = U
                       // super-chunks of 256 weights per row per chunk)
-  int depth;          // lds_stage: chunks in flight per wave (2 or 3)
+  int depth;          // lds_stage: chunks in flight per wave (2, 3, 4 or 6)
+  int xregs;          // lds_stage: activations in registers (whole K in one launch, U = 1)
+  int cps;            // xregs: super-chunks per k-slice (1..4)
   int lpr_log2;       // log2(lanes sharing one weight row)
   int nu;             // units (of gemv_unit_weights weights) per row in this launch
   int64_t unit0;      // first unit of each row covered by this launch
@@ -40,6 +42,10 @@ struct GemvPlan {
 size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu);
 size_t gemv_mfma_reduce_bytes(int waves);  // extra LDS of an MFMA-mode launch
 size_t gemv_coal_stage_bytes(int u);        // per-workgroup staging of the coalesced MFMA kernel
+size_t gemv_coalr_lds_bytes();              // LDS of the coalesced kernel with activations in registers
+// whether a k-slice of cps super-chunks of `batch` activation rows can be
+// staged in one wave's chunk ring (the activations-in-registers kernel)
+bool gemv_coalr_fits(GemvFormat f, int cps, int batch);
 constexpr int kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 int gemv_unit_weights(GemvFormat f);
 int gemv_threads();

@@ -178,6 +178,35 @@ def test_q4_k_small(orc, N, K, B):
     assert_close(y, ref, TOL_QUANT, f"q4_k {N}x{K} b{B}")
 
 
+# Matrix-core coalesced kernel in both of its forms, forced through the
+# planner's tuning overrides: activations in registers (k-slices of one to
+# four 256-weight super-chunks, slices partly or wholly past the row end,
+# ragged tiles, up to 16 activation rows) and activations staged in LDS.
+COAL_CASES = [("q4_k", 17, 256, 3, {}), ("q4_k", 33, 768, 8, {}), ("q4_k", 100, 2304, 5, {}),
+              ("q4_k", 70, 7936, 16, {}), ("q4_k", 300, 8192, 8, {}),
+              ("q4_k", 40, 1024, 4, {"LQMM_TUNE_GEMV_KS": "1"}),
+              ("q4_k", 41, 2048, 6, {"LQMM_TUNE_GEMV_KS": "2"}),
+              ("q4_k", 129, 4096, 3, {"LQMM_TUNE_GEMV_KS": "4"}),
+              ("q4_0", 17, 256, 3, {}), ("q4_0", 33, 768, 16, {}), ("q4_0", 257, 2304, 4, {}),
+              ("q4_0", 70, 7936, 8, {}), ("q4_0", 71, 7936, 9, {}), ("q4_0", 300, 4096, 4, {}),
+              ("q4_0", 40, 1024, 8, {"LQMM_TUNE_GEMV_KS": "1"}),
+              ("q4_0", 65, 3072, 5, {"LQMM_TUNE_GEMV_KS": "2"})]
+
+
+@pytest.mark.parametrize("xregs", [0, 1])
+@pytest.mark.parametrize("fmt,N,K,B,env", COAL_CASES)
+def test_coal_forms(orc, monkeypatch, xregs, fmt, N, K, B, env):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_XREGS", str(xregs))  # 1 forces it where it fits
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(N, K, B, seed=N + K * 3 + B + xregs)
+    announce(f"{fmt} gemv N={N} K={K} batch={B} xregs={xregs} {env}")
+    y = _run_q4_k(c) if fmt == "q4_k" else _run_q4_0(c)
+    ref = (orc.gemv_q4_k if fmt == "q4_k" else orc.gemv_q4_0)(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"{fmt} {N}x{K} b{B} xregs={xregs} {env}")
+
+
 @pytest.mark.parametrize("name", ["q4_k_gemv_28672x8192_b1", "q4_k_gemv_28672x8192_b8"])
 def test_q4_k_configs(orc, name):
     c = synth.make(name)
