@@ -263,7 +263,9 @@ Q8_0_SMALL = [(1, 1, 32), (3, 5, 64), (17, 130, 96), (128, 128, 64), (130, 257, 
               (64, 200, 4096), (256, 512, 1024), (1, 300, 32),
               # ragged in every dimension at once: partial output tiles and a
               # last K step holding a single block
-              (129, 257, 160), (300, 513, 224), (512, 768, 4128)]
+              (129, 257, 160), (300, 513, 224), (512, 768, 4128),
+              # odd numbers of 64-wide K steps
+              (70, 300, 192), (33, 257, 448)]
 
 
 @pytest.mark.parametrize("M,N,K", Q8_0_SMALL)
