@@ -22,7 +22,14 @@ Reported (one JSON line on stdout):
   prefill_gemm   Q8_0 x fp16 GEMM TFLOP/s against the 2.5 PFLOP/s f16 peak;
   fp32_gemm      fp32 GEMM TFLOP/s against the 157.3 TFLOP/s fp32 peak;
   cases          every call timed alone: kernel time, GB/s or TFLOP/s;
-  cpu_baseline   the fp64 CPU oracle on the same GEMV inputs (host cores).
+  context        measured after the timed steps, for reading the figures
+                 above: a plain streaming-read kernel over the Q4_K weight
+                 copies (the HBM rate a simple kernel reaches here), every
+                 GEMV on one weight copy back to back (cache-resident, not
+                 HBM), and the host wall time per call of the smallest GEMVs
+                 called one by one (launch overhead included);
+  cpu_baseline   the fp64 CPU oracle on the same GEMV inputs (host cores),
+                 with a shorter one-thread sample and the host CPU model.
 
 Algorithmic bytes count the packed weights, the activations and the outputs,
 each moved once; flops are 2*M*N*K.
@@ -89,10 +96,11 @@ class Rot:
 
 
 class Case:
-    def __init__(self, name, kind, bytes_, flops, launch, nrot, make_out):
+    def __init__(self, name, kind, bytes_, flops, launch, nrot, make_out, launch_warm=None):
         self.name, self.kind = name, kind
         self.bytes, self.flops = bytes_, flops
         self.launch = launch          # launch(): one call on the next weight copy
+        self.launch_warm = launch_warm  # one call on the same weight copy every time
         self.nrot = nrot
         self.make_out = make_out      # host array of the last output
         self.avg_ms = None
@@ -107,6 +115,7 @@ def build_cases(torch, only):
     dev = torch.device("cuda:0")
     cases = []
     inputs = {}  # for the CPU-baseline / parity leg
+    stream_sets = {}  # weight copies the streaming-read probe reads
 
     def rot(nbytes):
         return max(2, math.ceil(ROTATE_BYTES / nbytes))
@@ -139,8 +148,11 @@ def build_cases(torch, only):
             def launch(Ws=Ws, x=x, y=y, N=N):
                 bq.lqmm_gemv_q4_0(Ws.next(), x, N, out=y)
 
+            def launch_warm(W0=Ws.copies[0], x=x, y=y, N=N):
+                bq.lqmm_gemv_q4_0(W0, x, N, out=y)
+
             cases.append(Case(name, "gemv", alg, 2 * b * N * 4096, launch, R,
-                              lambda y=y: y.cpu().numpy()))
+                              lambda y=y: y.cpu().numpy(), launch_warm))
             inputs[name] = ("q4_0", c4.W, c4.x[:b].copy(), N, 4096)
 
     # Q4_K decode GEMV at the 70B FFN shape, batch 1 and 8
@@ -160,9 +172,13 @@ def build_cases(torch, only):
             def launch(Ws=Ws, x=x, y=y, N=ck.N):
                 bq.lqmm_gemv_q4_k(Ws.next(), x, N, out=y)
 
+            def launch_warm(W0=Ws.copies[0], x=x, y=y, N=ck.N):
+                bq.lqmm_gemv_q4_k(W0, x, N, out=y)
+
             cases.append(Case(name, "gemv", alg, 2 * b * ck.N * ck.K, launch, R,
-                              lambda y=y: y.cpu().numpy()))
+                              lambda y=y: y.cpu().numpy(), launch_warm))
             inputs[name] = ("q4_k", ck.W, ck.x[:b].copy(), ck.N, ck.K)
+        stream_sets["q4_k_28672x8192"] = Ws
 
     # Q8_0 x fp16 prefill GEMM
     name = "q8_0_gemm_512x14336x4096"
@@ -199,7 +215,7 @@ def build_cases(torch, only):
         cases.append(Case(name, "gemm_f32", alg, 2 * s.M * s.N * s.K, launch, R,
                           lambda C=C: C.cpu().numpy()))
         inputs[name] = ("sgemm", s.A, s.B, s.N, s.K)
-    return cases, inputs
+    return cases, inputs, stream_sets
 
 
 def capture(torch, fn):
@@ -241,37 +257,132 @@ def traffic_for(case_name):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inputs, gpu_outputs, min_seconds):
     """The fp64 CPU oracle on the same host bytes as the GPU GEMV calls: all
     rows of every call, repeated until at least `min_seconds` of wall time
-    (a bounded sample), plus a parity check of the GPU outputs against it."""
+    (a bounded sample), plus a parity check of the GPU outputs against it;
+    then a shorter sample on one thread."""
     import oracle
 
     orc = oracle.get()
     gemv = [(n, v) for n, v in inputs.items() if v[0] in ("q4_0", "q4_k")]
     if not gemv:
         return None, None
-    tot_bytes, passes, worst = 0, 0, 0.0
-    t0 = time.perf_counter()
-    while True:
-        for name, (fmt, W, x, N, K) in gemv:
-            ref = orc.gemv_q4_0(W, x, N, K) if fmt == "q4_0" else orc.gemv_q4_k(W, x, N, K)
-            b = x.shape[0]
-            tot_bytes += W.nbytes + b * K * 4 + b * N * 4
-            if passes == 0 and name in gpu_outputs:
-                rel, nmax = oracle.errors(gpu_outputs[name], ref)
-                worst = max(worst, rel, nmax)
-        passes += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    tot_s = time.perf_counter() - t0
+
+    def sample(seconds, check):
+        tot_bytes, passes, worst = 0, 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            for name, (fmt, W, x, N, K) in gemv:
+                ref = orc.gemv_q4_0(W, x, N, K) if fmt == "q4_0" else orc.gemv_q4_k(W, x, N, K)
+                b = x.shape[0]
+                tot_bytes += W.nbytes + b * K * 4 + b * N * 4
+                if check and passes == 0 and name in gpu_outputs:
+                    rel, nmax = oracle.errors(gpu_outputs[name], ref)
+                    worst = max(worst, rel, nmax)
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        return tot_bytes, passes, time.perf_counter() - t0, worst
+
+    threads = orc.threads
+    tot_bytes, passes, tot_s, worst = sample(min_seconds, True)
+    orc.set_threads(1)
+    b1, p1, s1, _ = sample(min_seconds / 4, False)
+    orc.set_threads(threads)
     names = ", ".join(n for n, _ in gemv)
-    return ({"value": round(tot_bytes / tot_s / 1e9, 3), "unit": "GB/s", "cores": orc.threads,
+    return ({"value": round(tot_bytes / tot_s / 1e9, 3), "unit": "GB/s", "cores": threads,
              "kind": "oracle",
              "sample": f"{passes} passes over all rows of the step's {len(gemv)} GEMV calls "
-                       f"({names}); {tot_s:.1f} s wall on {orc.threads} threads; fp64 "
-                       "dequantize-then-multiply"},
+                       f"({names}); {tot_s:.1f} s wall on {threads} threads; fp64 "
+                       "dequantize-then-multiply",
+             "single_thread": {"value": round(b1 / s1 / 1e9, 3), "unit": "GB/s",
+                               "sample": f"{p1} passes, {s1:.1f} s wall on 1 thread"},
+             "cpu_model": cpu_model()},
             worst)
+
+
+def measure_context(torch, cases, stream_sets, steps):
+    """Context figures, taken after the timed steps (see the module doc)."""
+    import ctypes
+
+    import block_quantized_matmul_amd as bq
+
+    ctx = {}
+
+    def graph_ms(fn, n):
+        g = capture(torch, lambda: [fn() for _ in range(n)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # Plain streaming read over the rotated Q4_K weight copies.
+    probe = os.path.join(ROOT, "block_quantized_matmul_amd", "liblqmm_probe.so")
+    ws = stream_sets.get("q4_k_28672x8192")
+    if ws is not None and os.path.exists(probe):
+        lib = ctypes.CDLL(probe)
+        lib.lqmm_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                               ctypes.c_int, ctypes.c_void_p]
+        lib.lqmm_probe_stream_read.restype = ctypes.c_int
+        out = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+        nbytes = ws.copies[0].numel() * ws.copies[0].element_size()
+        best = None
+        for grid in (1024, 2048, 4096):
+            def rd(grid=grid):
+                t = ws.next()
+                rc = lib.lqmm_probe_stream_read(t.data_ptr(), nbytes, out.data_ptr(), grid,
+                                                torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"streaming-read probe failed: {rc}")
+            ms = graph_ms(rd, steps)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, grid, ms)
+        ctx["hbm_stream"] = {"gbs": round(best[0], 1), "frac": round(best[0] / HBM_PEAK_GBS, 4),
+                             "bytes": nbytes, "ms": round(best[2], 6), "grid": best[1],
+                             "kernel": "grid-stride 16-byte non-temporal reads, 8 in flight per "
+                                       "thread, over the rotated Q4_K weight copies (cold HBM); "
+                                       "best of grids 1024, 2048, 4096"}
+    # GEMVs on one weight copy back to back: cache-resident, not HBM.
+    warm = {}
+    for c in cases:
+        if c.kind == "gemv" and c.launch_warm is not None:
+            ms = graph_ms(c.launch_warm, steps)
+            warm[c.name] = {"ms": round(ms, 6), "gbs": round(c.bytes / (ms * 1e-3) / 1e9, 1)}
+    if warm:
+        ctx["warm_same_copy"] = warm
+    # Host wall time per call, one call at a time (binding and launch included).
+    calls = {}
+    for c in cases:
+        if c.name in ("q4_0_gemv_4096x4096_b1", "q4_0_gemv_4096x4096_b4"):
+            for _ in range(20):
+                c.launch()
+            torch.cuda.synchronize()
+            n = 200
+            t0 = time.perf_counter()
+            for _ in range(n):
+                c.launch()
+            torch.cuda.synchronize()
+            calls[c.name] = round((time.perf_counter() - t0) / n * 1e6, 2)
+    if calls:
+        ctx["host_wall_us_per_call"] = calls
+    return ctx
 
 
 # ---- rocprofv3 summaries (host only) -------------------------------------------
@@ -373,7 +484,7 @@ def main():
     only = set(s for s in args.cases.split(",") if s)
 
     t_setup = time.perf_counter()
-    cases, inputs = build_cases(torch, only)
+    cases, inputs, stream_sets = build_cases(torch, only)
     torch.cuda.synchronize()
     print(f"[bench] {len(cases)} cases set up in {time.perf_counter() - t_setup:.1f} s",
           file=sys.stderr, flush=True)
@@ -474,6 +585,7 @@ def main():
             line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
                          "ms": round(gc.avg_ms, 6)}
     line["cases"] = {c.name: case_summary(c) for c in order}
+    line["context"] = measure_context(torch, cases, stream_sets, args.steps)
 
     if not args.no_cpu_baseline:
         base, worst = cpu_baseline(inputs, gpu_out, args.cpu_seconds)

@@ -1,0 +1,47 @@
+// Streaming-read probe: the HBM read rate a plain kernel reaches on this GPU,
+// reported by the benchmark as context for the GEMV kernels' rates (which are
+// judged against the 8 TB/s datasheet peak). Every 16-byte word of the buffer
+// is read once, grid-stride, with non-temporal loads, eight words in flight
+// per thread. Built as its own library (liblqmm_probe.so); not part of the
+// lqmm interface.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kDepth = 8;
+
+__global__ void __launch_bounds__(kThreads)
+stream_read_kernel(const u32x4 *__restrict__ p, int64_t n16, uint32_t *out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kDepth - 1) * stride < n16; i += kDepth * stride) {
+    u32x4 v[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // The loads must not be optimized away; this store almost never happens.
+  if (acc == 0x9E3779B9u) out[0] = acc;
+}
+
+}  // namespace
+
+// Read `bytes` (a multiple of 16) from the 16-byte aligned device buffer p on
+// `stream` with `grid` workgroups of 256 threads; `out` is a device word the
+// kernel may write. Returns 0, or the HIP error code of the launch.
+extern "C" int lqmm_probe_stream_read(const void *p, int64_t bytes, void *out, int grid,
+                                      void *stream) {
+  if (!p || !out || bytes < 16 || bytes % 16 != 0 || grid < 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     static_cast<const u32x4 *>(p), bytes / 16, static_cast<uint32_t *>(out));
+  return (int)hipGetLastError();
+}

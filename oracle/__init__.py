@@ -58,12 +58,18 @@ class Oracle:
         lib.lqmm_oracle_sgemm.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
         lib.lqmm_oracle_mutant.restype = ctypes.c_int
         lib.lqmm_oracle_threads.restype = ctypes.c_int
+        lib.lqmm_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.lqmm_oracle_set_threads.restype = None
         self.lib = lib
 
     @property
     def threads(self) -> int:
         """OpenMP threads the oracle's loops use."""
         return self.lib.lqmm_oracle_threads()
+
+    def set_threads(self, n: int) -> None:
+        """Run the oracle's loops on n OpenMP threads."""
+        self.lib.lqmm_oracle_set_threads(int(n))
 
     @property
     def mutant(self) -> int:

@@ -309,5 +309,11 @@ void lqmm_oracle_sgemm(const float *A, const float *B, double *C, int64_t M, int
 /* Threads the OpenMP loops above use. */
 int lqmm_oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Set the threads of the loops above (n >= 1); used to time the oracle on
+   one core as well as on all of them. */
+void lqmm_oracle_set_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+}
+
 /* Mutant id this library was built with (0 = the real oracle). */
 int lqmm_oracle_mutant(void) { return LQMM_ORACLE_MUTANT; }
