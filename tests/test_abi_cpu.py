@@ -45,6 +45,16 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(bq.EXPORTS) == set(_declared())
 
 
+def test_probe_library_loads(lib):
+    # the bench's streaming-read probe: its own library, built with liblqmm.so
+    probe = os.path.join(os.path.dirname(bq.library_path()), "liblqmm_probe.so")
+    assert os.path.exists(probe)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe],
+                         capture_output=True, text=True, check=True).stdout
+    assert re.search(r"\bT lqmm_probe_stream_read$", out, flags=re.M)
+    ctypes.CDLL(probe).lqmm_probe_stream_read
+
+
 def test_library_does_not_link_the_oracle(lib):
     out = subprocess.run(["nm", "-D", bq.library_path()], capture_output=True, text=True).stdout
     assert "oracle" not in out
