@@ -26,8 +26,10 @@ Reported (one JSON line on stdout):
                  above: a plain streaming-read kernel over the Q4_K weight
                  copies (the HBM rate a simple kernel reaches here), every
                  GEMV on one weight copy back to back (cache-resident, not
-                 HBM), and the host wall time per call of the smallest GEMVs
-                 called one by one (launch overhead included);
+                 HBM), the host wall time per call of the smallest GEMVs
+                 called one by one (launch overhead included), and the
+                 vendor library's GEMMs at the same shapes (torch.matmul on
+                 hipBLASLt: fp16 with dense fp16 weights, and fp32);
   cpu_baseline   the fp64 CPU oracle on the same GEMV inputs (host cores),
                  with a shorter one-thread sample and the host CPU model.
 
@@ -322,6 +324,9 @@ def measure_context(torch, cases, stream_sets, steps):
     ctx = {}
 
     def graph_ms(fn, n):
+        for _ in range(3):  # outside the capture: library set-up (hipBLASLt's) and warm-up
+            fn()
+        torch.cuda.synchronize()
         g = capture(torch, lambda: [fn() for _ in range(n)])
         g.replay()
         torch.cuda.synchronize()
@@ -382,6 +387,44 @@ def measure_context(torch, cases, stream_sets, steps):
             calls[c.name] = round((time.perf_counter() - t0) / n * 1e6, 2)
     if calls:
         ctx["host_wall_us_per_call"] = calls
+    # The vendor library's GEMMs at the same shapes (reference points, not
+    # this library): dense fp16 weights (twice the Q8_0 bytes), rotated cold
+    # copies; and the fp32 GEMM.
+    vend = {}
+    gq = next((c for c in cases if c.name == "q8_0_gemm_512x14336x4096"), None)
+    if gq is not None:
+        M, N, K = 512, 14336, 4096
+        X = torch.randn(M, K, dtype=torch.float16, device="cuda:0")
+        Y = torch.empty(M, N, dtype=torch.float16, device="cuda:0")
+        R = max(2, math.ceil(ROTATE_BYTES / (N * K * 2)))
+        Wf = Rot([torch.randn(N, K, dtype=torch.float16, device="cuda:0") for _ in range(R)])
+        ms = graph_ms(lambda: torch.matmul(X, Wf.next().t(), out=Y), steps)
+        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+        vend["fp16_gemm_512x14336x4096"] = {
+            "ms": round(ms, 6), "tflops": round(tf, 1), "frac": round(tf / F16_PEAK_TFLOPS, 4),
+            "call": "torch.matmul(X fp16 [512x4096], W fp16 [14336x4096] transposed view)"}
+        del Wf, X, Y
+    gs = next((c for c in cases if c.name == "sgemm_2048"), None)
+    if gs is not None:
+        n = 2048
+        R = max(2, math.ceil(ROTATE_BYTES / (2 * n * n * 4)))
+        AB = Rot([(torch.rand(n, n, device="cuda:0") * 2 - 1, torch.rand(n, n, device="cuda:0") * 2 - 1)
+                  for _ in range(R)])
+        C = torch.empty(n, n, device="cuda:0")
+
+        def mm():
+            A, B = AB.next()
+            torch.matmul(A, B, out=C)
+        ms = graph_ms(mm, steps)
+        tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        vend["fp32_gemm_2048"] = {"ms": round(ms, 6), "tflops": round(tf, 1),
+                                  "frac": round(tf / F32_PEAK_TFLOPS, 4),
+                                  "call": "torch.matmul(A fp32, B fp32), TF32 off",
+                                  "allow_tf32": bool(torch.backends.cuda.matmul.allow_tf32)}
+        del AB, C
+    if vend:
+        ctx["vendor_gemm"] = vend
+    torch.cuda.empty_cache()
     return ctx
 
 
@@ -585,7 +628,10 @@ def main():
             line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
                          "ms": round(gc.avg_ms, 6)}
     line["cases"] = {c.name: case_summary(c) for c in order}
-    line["context"] = measure_context(torch, cases, stream_sets, args.steps)
+    try:
+        line["context"] = measure_context(torch, cases, stream_sets, args.steps)
+    except Exception as e:  # context only: never costs the measurement above
+        line["context"] = {"error": f"{type(e).__name__}: {e}"}
 
     if not args.no_cpu_baseline:
         base, worst = cpu_baseline(inputs, gpu_out, args.cpu_seconds)
