@@ -325,17 +325,34 @@ struct FmtQ4_K {
   // MFMA mode: fp16 weights d*sc*q - dmin*m with d*sc and dmin*m each
   // rounded to fp16 once per sub-block, then one fused rounding per weight;
   // valid == false yields zero weights.
+  // Both sub-blocks are decoded at once as 16-bit lanes (sub-block 2*pair
+  // low, 2*pair + 1 high): their scale and min fields are bytes j and j + 1
+  // (j = 2*(pair & 1)) of the three scale words, 6-bit fields in words 1 and
+  // 2 for sub-blocks 0..3, 4 + 2 bits from words 3 and 1 (or 2) for 4..7.
+  // 1024 + v is exact in fp16, so v comes back exactly; the packed fp16
+  // products d*sc and dmin*m are the exact products rounded once, as above.
   static __device__ __forceinline__ Prep prep(const Raw &r, int pair, bool valid) {
-    float d = valid ? f16_bits_to_f32(r.h.x & 0xFFFF) : 0.0f;
-    float dmin = valid ? f16_bits_to_f32(r.h.x >> 16) : 0.0f;
-    uint32_t sc0, m0, sc1, m1;
-    scale_min(r.h, 2 * pair, sc0, m0);
-    scale_min(r.h, 2 * pair + 1, sc1, m1);
+    const uint32_t sel = (pair & 1) ? 0x0C030C02u : 0x0C010C00u;  // bytes j, j+1 -> 16-bit lanes
+    const uint32_t y = __builtin_amdgcn_perm(0u, r.h.y, sel);
+    const uint32_t z = __builtin_amdgcn_perm(0u, r.h.z, sel);
+    const uint32_t w = __builtin_amdgcn_perm(0u, r.h.w, sel);
+    const bool first = pair < 2;
+    const uint32_t m6 = first ? 0x003F003Fu : 0u, m2 = first ? 0u : 0x00300030u,
+                   m4 = first ? 0u : 0x000F000Fu;
+    const uint32_t sc = (y & m6) | ((y >> 2) & m2) | (w & m4);
+    const uint32_t mn = (z & m6) | ((z >> 2) & m2) | ((w >> 4) & m4);
+    const half2_t scv = as_half2(sc | kMagic) + h2(-1024.0f);
+    const half2_t mnv = as_half2(mn | kMagic) + h2(-1024.0f);
+    const uint32_t dd = valid ? r.h.x : 0u;
+    const half2_t d2 = as_half2(__builtin_amdgcn_perm(dd, dd, 0x01000100u));   // d, d
+    const half2_t dm2 = as_half2(__builtin_amdgcn_perm(dd, dd, 0x03020302u));  // dmin, dmin
+    const half2_t dsc = scv * d2;
+    const half2_t dmm = -(mnv * dm2);
     Prep p;
-    p.dsc_lo = h2(d * (float)sc0);
-    p.dmm_lo = h2(-dmin * (float)m0);
-    p.dsc_hi = h2(d * (float)sc1);
-    p.dmm_hi = h2(-dmin * (float)m1);
+    p.dsc_lo = dsc.xx;
+    p.dsc_hi = dsc.yy;
+    p.dmm_lo = dmm.xx;
+    p.dmm_hi = dmm.yy;
     return p;
   }
   static __device__ __forceinline__ u32x4 dequant(const Raw &r, const Prep &p, int t,
@@ -1085,19 +1102,23 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
 // <= 4 super-chunks. A wave's slice is the same for every tile it visits, so
 // it loads the fp16 A operands of its slice into registers once (32 VGPRs per
 // super-chunk; lanes whose batch row n >= nb hold zeros). LDS then holds only
-// a ring of DR chunk slots per wave, filled by buffer-to-LDS loads DR - 1
+// a ring of DR chunk slots per wave, filled by buffer-to-LDS loads up to DR
 // chunks ahead of the one being computed (no register round trip, no LDS
 // write instructions), and a k-split reduction area that alternates between
 // tiles, so that each tile needs one barrier.
 //
+// Order per chunk i: chunk i's slot was read into registers during chunk
+// i-1's arithmetic (so the LDS latency is hidden). The wave waits for those
+// reads, refills the slot with chunk i+DR, waits until chunk i+1 has landed,
+// issues the reads of chunk i+1, and then computes chunk i.
 // Waits: the compiler does not see the LDS data the buffer-to-LDS loads
-// write, so the wave waits for them explicitly. At the top of chunk i the
-// loads of chunks i+1 .. i+DR-1 (NI each) may stay in flight; loads return
-// in order. Stores to y issued after them are not counted, which can only
-// make the wait longer, never too short. A slot is refilled only after the
-// wave's reads of it have completed. Chunks past the end of the wave's work
-// are requested from an empty buffer range: they return zeros, touch no
-// memory, and keep the count of loads in flight constant.
+// write, so the wave waits for them explicitly. After the refill, the loads
+// of chunks i+2 .. i+DR (NI each) may stay in flight; loads return in order.
+// Stores to y issued after them are not counted, which can only make the
+// wait longer, never too short. A slot is refilled only after the wave's
+// reads of it have completed. Chunks past the end of the wave's work are
+// requested from an empty buffer range: they return zeros, touch no memory,
+// and keep the count of loads in flight constant.
 template <class C, int CPS, int KS, int DR>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,
@@ -1224,19 +1245,30 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
   float4_t acc = float4_t{0, 0, 0, 0};
   int par = 0;
   int cg = gfirst + team;  // tile being computed
+  // chunk 0's reads (the last of the DR requests may stay in flight)
+  typename F::Raw nx[LU];
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+#pragma unroll
+  for (int j = 0; j < LU; ++j)
+    nx[j] = C::read(reinterpret_cast<const u32x4 *>(ring) + n * PR, q, j);
   for (int tt = 0; tt < n_tiles; ++tt) {
 #pragma unroll
     for (int c = 0; c < CPS; ++c) {
-      // keep the previous chunk's work ahead of this chunk's wait
+      // keep the previous chunk's work ahead of this chunk's waits
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
-      const u32x4 *wbuf = reinterpret_cast<const u32x4 *>(ring + slot * kSlot);
       typename F::Raw rw[LU];
 #pragma unroll
-      for (int j = 0; j < LU; ++j) rw[j] = C::read(wbuf + n * PR, q, j);
+      for (int j = 0; j < LU; ++j) rw[j] = nx[j];
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(slot);
       slot = slot + 1 == DR ? 0 : slot + 1;
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+      {
+        // past the wave's last chunk this reads a slot of zeros: harmless
+        const u32x4 *wbuf = reinterpret_cast<const u32x4 *>(ring + slot * kSlot);
+#pragma unroll
+        for (int j = 0; j < LU; ++j) nx[j] = C::read(wbuf + n * PR, q, j);
+      }
       const bool valid = sc0 + c < nsc;
 #pragma unroll
       for (int j = 0; j < LU; ++j) {
