@@ -432,9 +432,21 @@ def measure_context(torch, cases, stream_sets, steps):
 
 def _short_kernel(name):
     import re
-    name = re.sub(r"lqmm::\(anonymous namespace\)::", "", name)
-    name = re.sub(r"\(.*\)$", "", name)
-    return name.replace("void ", "")
+    name = re.sub(r"\(anonymous namespace\)::", "", name).replace("lqmm::", "")
+    name = name.replace("void ", "")
+    if name.endswith(")"):  # drop the argument list (the last balanced parentheses)
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    if name.startswith("Cijk_"):  # vendor GEMM kernels: keep the tile part of the name
+        m = re.search(r"_MT\w+?_MI\w+?_", name)
+        name = "vendor GEMM " + name.split("_")[1] + (" " + m.group(0).strip("_") if m else "")
+    elif name.startswith("at::"):  # torch's set-up kernels: their template name only
+        name = name.split("<")[0] + " (torch)"
+    return name
 
 
 def summarize_trace(stats_csv, out_md, command, title):
