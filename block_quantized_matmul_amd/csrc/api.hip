@@ -76,6 +76,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   const int env_depth = env_int("LQMM_TUNE_GEMV_DEPTH");
   const int env_pair = env_int("LQMM_TUNE_GEMV_Q4_0_PAIR");
   const int env_xregs = env_int("LQMM_TUNE_GEMV_XREGS");
+  const int env_stream = env_int("LQMM_TUNE_GEMV_STREAM");
   const int64_t tiles = (N + 15) / 16;  // 16-row tiles of the matrix-core kernels
 
   // K-slices per tile of the coalesced kernel (one workgroup per CU): the
@@ -150,6 +151,20 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       const int64_t tiles_per_wave = (tiles + grid * (8 / ks) - 1) / (grid * (8 / ks));
       if (env_xregs != 1) xregs = xregs && tiles_per_wave * cps >= 12;
     }
+    // Batch-1 Q4_K with rows of at most 8192 weights streams its rows through
+    // LDS (one workgroup per CU, whole K in one launch, a chunk ring two deep)
+    // when every wave gets at least two rows. Measured: 4% faster at
+    // 28672 x 8192 and 8% at 14336 x 4096, even at 8192 x 8192 (two rows per
+    // wave), 4% slower at 4096 x 4096 (one). Tuning override: 0 off, 1 on
+    // whatever N is, 2 or 3 on with that ring depth.
+    int streamed = 0;
+    if (fmt == GemvFormat::Q4_K && B == 1 && env_stream != 0 &&
+        units <= lqmm::gemv_stream_max_units()) {
+      const int64_t waves_total = (int64_t)num_cus * lqmm::gemv_stream_waves();
+      int dr = env_stream == 3 ? 3 : 2;
+      if (env_stream >= 1 || N >= 2 * waves_total)
+        streamed = lqmm::gemv_stream_lds_bytes((int)units, dr) <= (size_t)lqmm::kMaxLds ? dr : 0;
+    }
     // Other MFMA launches: 16-wave workgroups when the staged activations
     // leave room for only one workgroup per CU, so that more loads are in
     // flight.
@@ -176,7 +191,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     const int64_t lds_cap = lds_stage ? lqmm::kMaxLds : lqmm::kMaxGemvLds;
     // per-unit cost taken over many units, where the row padding is negligible
     int64_t max_units = units;
-    if (!xregs) {
+    if (!xregs && !streamed) {
       max_units = (lds_cap - red_bytes) * 4096 / (int64_t)lqmm::gemv_lds_bytes(f, mfma, B, 4096);
       // K-split launches start on whole Q4_K super-blocks, and on whole
       // super-chunks for the coalesced kernel.
@@ -197,12 +212,13 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       int lpr_log2 = 0;
       while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
       pl.lpr_log2 = lpr_log2;
-      pl.lds_bytes = xregs ? lqmm::gemv_coalr_lds_bytes()
-                           : lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
+      pl.lds_bytes = xregs    ? lqmm::gemv_coalr_lds_bytes()
+                     : streamed ? lqmm::gemv_stream_lds_bytes(nu, streamed)
+                              : lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
       int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
       // The coalesced kernel runs one workgroup per CU: each workgroup stages
       // all of x, so more workgroups mostly add staging traffic.
-      const int64_t wg_cap = env_wgcu > 0 ? env_wgcu : (lds_stage ? 1 : 2);
+      const int64_t wg_cap = env_wgcu > 0 ? env_wgcu : (lds_stage || streamed ? 1 : 2);
       if (wg_per_cu > wg_cap) wg_per_cu = wg_cap;
       if (wg_per_cu < 1) wg_per_cu = 1;
       int64_t wg_needed;
@@ -226,6 +242,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         pl.lds_stage = lds_stage;
         pl.xregs = xregs;
         pl.cps = xregs ? (nu / sc_units + ks - 1) / ks : 0;
+        pl.stream = 0;
         pl.depth = (env_depth == 2 || env_depth == 3 || env_depth == 4 || env_depth == 6) ? env_depth : 2;
         const int teams = waves / ks;
         wg_needed = (tiles + teams - 1) / teams;
@@ -245,8 +262,11 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         pl.xregs = 0;
         pl.cps = 0;
         pl.depth = 2;
-        const int64_t groups = (N + (int64_t)slots * r - 1) / ((int64_t)slots * r);
-        wg_needed = (groups + waves_per_wg - 1) / waves_per_wg;
+        pl.stream = streamed;
+        // the streamed kernel: one row per wave at a time
+        const int64_t groups = streamed ? N : (N + (int64_t)slots * r - 1) / ((int64_t)slots * r);
+        const int wpw = streamed ? lqmm::gemv_stream_waves() : waves_per_wg;
+        wg_needed = (groups + wpw - 1) / wpw;
       }
       pl.nu = nu;
       pl.unit0 = u0;

@@ -267,11 +267,21 @@ struct FmtQ4_K {
   static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
                                                  const float *sums, int u, int nu, bool valid,
                                                  const UnpackMasks &k, float (&acc)[R][B]) {
+    compute_with<B, R>(
+        raw, [&](int b, int t) { return xs[(b * kWords + t) * xstride + u]; },
+        [&](int b, int h) { return sums[2 * (b * nu + u) + h]; }, u, valid, k, acc);
+  }
+  // The same with the unit's staged words and sums taken from xword(b, t)
+  // and sum(b, h) (h = 0: lo, 1: hi), wherever the caller keeps them.
+  template <int B, int R, class XW, class SW>
+  static __device__ __forceinline__ void compute_with(const Raw (&raw)[R], XW xword, SW sum, int u,
+                                                      bool valid, const UnpackMasks &k,
+                                                      float (&acc)[R][B]) {
     float slo[R][B], shi[R][B], nsl[B], nsh[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      nsl[b] = sums[2 * (b * nu + u)];
-      nsh[b] = sums[2 * (b * nu + u) + 1];
+      nsl[b] = sum(b, 0);
+      nsh[b] = sum(b, 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         slo[r][b] = nsl[b];
@@ -282,7 +292,7 @@ struct FmtQ4_K {
     for (int t = 0; t < kWords; ++t) {
       u32x4 X[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * xstride + u];
+      for (int b = 0; b < B; ++b) X[b] = xword(b, t);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         Nibbles n = unpack_word(word(raw[r], t), k);
@@ -1311,10 +1321,198 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---- VALU mode, weight rows streamed through LDS ------------------------------
+// Batch-1 Q4_K GEMV (K <= 8192) whose weights reach each wave as contiguous
+// chunks: a chunk (16 super-blocks of one row, 2304 bytes) is copied into a
+// wave-private LDS ring slot by buffer-to-LDS loads of 64 x 16 consecutive
+// bytes, with non-temporal hints (every byte is read once), up to DR chunks
+// ahead. Lane l then reads unit l of the chunk from the slot (the
+// super-block header and the unit's two 16-byte quant pieces) and uses the
+// dot2 arithmetic of gemv_kernel. Every load instruction covers 1 KB of one
+// row; gemv_kernel's unit-shaped loads put lanes 32 bytes apart and read
+// each header line from four lanes, which rules out non-temporal loads.
+// Lane l always takes units l, l + 64, ... of a row (chunk c holds units
+// 64c .. 64c + 63), so after the workgroup has staged x it keeps the staged
+// words and sums of its first unit in registers: for rows of up to 4096
+// weights the LDS then serves only the weight chunks. Sixteen waves per workgroup, one workgroup per CU; waves
+// take whole rows, row r by wave r mod (waves in the grid). The first chunks
+// are requested before the staging (the ring does not overlap the staged
+// activations), and a chunk's units are read from LDS during the previous
+// chunk's arithmetic.
+// Waits: as in gemv_coalr_kernel (loads return in order; a slot is refilled
+// only after the wave's reads of it are complete; chunks past the wave's
+// work come from an empty buffer range).
+constexpr int kStreamWaves = 16;
+constexpr int kStreamThreads = kStreamWaves * kWave;
+constexpr int kStreamChunkSB = 16;                 // super-blocks per chunk (144 B each)
+constexpr int kStreamSlot = kStreamChunkSB * 144;  // 2304 bytes
+constexpr int kStreamLoads = (kStreamSlot + kWave * 16 - 1) / (kWave * 16);  // 3 (the last 256 B)
+constexpr int kStreamMaxUPL = 2;                   // chunks (units per lane) per row: K <= 8192
+static_assert(kStreamChunkSB * 4 == kWave, "one unit per lane");
+
+template <class F>
+__host__ __device__ __forceinline__ size_t stream_stage_bytes(int nu) {
+  const size_t b = (size_t)F::kWords * staged_stride<F>(nu) * 16 + (size_t)nu * F::kSums * 4;
+  return (b + 15) & ~(size_t)15;
+}
+
+template <class F, int UPL, int DR>
+__global__ void __launch_bounds__(kStreamThreads)
+gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
+                   const float *__restrict__ x, float *__restrict__ y, int64_t N) {
+  constexpr int T = F::kWords;
+  constexpr int NI = kStreamLoads;
+  static_assert((DR - 1) * NI <= 63, "load counter range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot t*NS + u
+  const int NS = staged_stride<F>(nu);
+  float *sums = reinterpret_cast<float *>(smem + (size_t)T * NS * 16);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  uint8_t *const ring = smem + stream_stage_bytes<F>(nu) + (size_t)wave * DR * kStreamSlot;
+  const int nsb = nu / 4;  // super-blocks per row: UPL - 1 full chunks and a last one
+  const int64_t nwaves = (int64_t)gridDim.x * kStreamWaves;
+  const int64_t wave_id = (int64_t)blockIdx.x * kStreamWaves + wave;
+  const int64_t n_rows = wave_id < N ? (N - wave_id + nwaves - 1) / nwaves : 0;
+  auto chunk_units = [&](int c) {  // units in chunk c of a row
+    return 4 * (nsb - c * kStreamChunkSB < kStreamChunkSB ? nsb - c * kStreamChunkSB
+                                                          : kStreamChunkSB);
+  };
+
+  // Request item `issued` (chunk ic of row irow) into ring slot `slot`.
+  int64_t irow = wave_id, issued = 0;
+  int ic = 0;
+  auto issue = [&](int slot) {
+    const bool live = issued < n_rows * UPL;
+    const int64_t r = irow < N ? irow : N - 1;
+    const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * (kStreamChunkSB * 144),
+                                live ? (uint32_t)(chunk_units(ic) * 36) : 0u);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      // the last load covers the slot's tail only: its other lanes are
+      // switched off, so that nothing is written past the slot
+      if ((k + 1) * kWave * 16 <= kStreamSlot || lane * 16 < kStreamSlot - k * kWave * 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring + slot * kStreamSlot + k * (kWave * 16),
+                                                 16, k * (kWave * 16) + lane * 16, 0, 0, 2 /* nt */);
+    }
+    ++issued;
+    if (++ic == UPL) {
+      ic = 0;
+      irow += nwaves;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < DR; ++k) issue(k);
+
+  // Stage the activation words, then the per-unit sums, as gemv_kernel does;
+  // then each lane copies those of its units into registers. The barriers
+  // wait for LDS operations only, not for the chunk requests above.
+  stage_words<F, kStreamThreads, 1>(xs, 1, nu, x, nu * F::kUnitWeights, 0.0625f,
+                                    [&](int, int u, int t) { return t * NS + u; });
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int u = tid; u < nu; u += kStreamThreads) {
+#pragma unroll
+    for (int g = 0; g < T / F::kSumWords; ++g) {
+      float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+      for (int t = g * F::kSumWords; t < (g + 1) * F::kSumWords; ++t)
+        word_sums(xs[t * NS + u], slo, shi);
+      F::stage_sums(sums, u, g, slo, shi);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // Registers hold the first chunk's activations; those of a second chunk
+  // stay in LDS (there are no registers left for them).
+  u32x4 xr[T];
+  float sr[2];
+  {
+    const int u = lane < nu ? lane : nu - 1;
+#pragma unroll
+    for (int t = 0; t < T; ++t) xr[t] = xs[t * NS + u];
+    sr[0] = sums[2 * u];
+    sr[1] = sums[2 * u + 1];
+  }
+
+  // Lane's unit of the chunk in `slot` (clamped into the chunk).
+  auto read_unit = [&](int slot, int nuc, typename F::Raw &r) {
+    const u32x4 *wb = reinterpret_cast<const u32x4 *>(ring + slot * kStreamSlot);
+    const int uc = lane < nuc ? lane : nuc - 1;
+    const u32x4 *sbp = wb + (uc >> 2) * 9;
+    r.h = sbp[0];
+    r.q0 = sbp[1 + 2 * (uc & 3)];
+    r.q1 = sbp[2 + 2 * (uc & 3)];
+  };
+
+  // The next chunk's unit is read early (during this chunk's arithmetic).
+  constexpr bool kEarly = true;
+  const UnpackMasks kmask;
+  int slot = 0;
+  typename F::Raw nx[1];
+  if (kEarly) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+    read_unit(0, chunk_units(0), nx[0]);
+  }
+  int64_t crow = wave_id;
+  for (int64_t rr = 0; rr < n_rows; ++rr) {
+    float acc[1][1] = {{0.0f}};
+#pragma nounroll
+    for (int c = 0; c < UPL; ++c) {
+      __builtin_amdgcn_sched_barrier(0);
+      typename F::Raw rw[1];
+      if (kEarly) {
+        rw[0] = nx[0];
+      } else {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+        read_unit(slot, chunk_units(c), rw[0]);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(slot);
+      slot = slot + 1 == DR ? 0 : slot + 1;
+      if (kEarly) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+        // past the wave's last chunk this reads a slot of zeros: harmless
+        read_unit(slot, chunk_units(0), nx[0]);
+      }
+      const int nuc = chunk_units(c);
+      const bool valid = lane < nuc;
+      const int u = c * kWave + (valid ? lane : 0);
+      if (c == 0)
+        F::template compute_with<1, 1>(
+            rw, [&](int, int t) { return xr[t]; }, [&](int, int h) { return sr[h]; }, u, valid,
+            kmask, acc);
+      else
+        F::template compute<1, 1>(rw, xs, NS, sums, u, nu, valid, kmask, acc);
+    }
+    const float v = group_sum(acc[0][0], kWave);
+    if (lane == kWave - 1) y[crow] = v;
+    crow += nwaves;
+  }
+  // no buffer-to-LDS load may be left in flight when the wave ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <class K>
 hipError_t set_lds_attr(K kern) {
   return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxGemvLds);
+}
+
+template <class F, int UPL, int DR>
+hipError_t launch_stream(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                         hipStream_t stream) {
+  auto kern = gemv_stream_kernel<F, UPL, DR>;
+  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kStreamThreads), pl.lds_bytes, stream, W,
+                     pl.row_bytes, pl.nu, x, y, pl.N);
+  return hipGetLastError();
 }
 
 template <class F, int B, int R, int U, bool FULL>
@@ -1489,6 +1687,17 @@ hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, floa
   } else {
     if (pl.mfma) return launch_fmt_mfma<F>(pl, W, x, y, s);
   }
+  if constexpr (std::is_same<F, FmtQ4_K>::value) {
+    if (pl.stream) {
+      // batch 1, the whole row in one launch, at most kStreamMaxUPL chunks
+      const int upl = (pl.nu / 4 + kStreamChunkSB - 1) / kStreamChunkSB;
+      if (pl.batch != 1 || pl.unit0 != 0 || pl.accumulate || upl > kStreamMaxUPL)
+        return hipErrorInvalidValue;
+      if (pl.stream == 3)
+        return upl == 1 ? launch_stream<F, 1, 3>(pl, W, x, y, s) : launch_stream<F, 2, 3>(pl, W, x, y, s);
+      return upl == 1 ? launch_stream<F, 1, 2>(pl, W, x, y, s) : launch_stream<F, 2, 2>(pl, W, x, y, s);
+    }
+  }
   const bool full = pl.lpr_log2 == 6;
   if (pl.batch == 1)
     return full ? launch_ru<F, 1, true>(pl, W, x, y, s) : launch_ru<F, 1, false>(pl, W, x, y, s);
@@ -1524,6 +1733,14 @@ bool gemv_coalr_fits(GemvFormat f, int cps, int batch) {
 size_t gemv_coalr_lds_bytes() {
   return (size_t)kWavesPerWg * kCoalrRing * 3 * kWave * 16 + (size_t)2 * kWavesPerWg * kWave * 16;
 }
+
+size_t gemv_stream_lds_bytes(int nu, int depth) {
+  return stream_stage_bytes<FmtQ4_K>(nu) + (size_t)kStreamWaves * depth * kStreamSlot;
+}
+
+int gemv_stream_max_units() { return kStreamMaxUPL * kStreamChunkSB * 4; }
+
+int gemv_stream_waves() { return kStreamWaves; }
 
 size_t gemv_coal_stage_bytes(int u) {
   return (size_t)kWavesPerWg * ((16 * 9 * u + 63) / 64) * kWave * 16;

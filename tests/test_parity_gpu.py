@@ -207,6 +207,41 @@ def test_coal_forms(orc, monkeypatch, xregs, fmt, N, K, B, env):
     assert_close(y, ref, TOL_QUANT, f"{fmt} {N}x{K} b{B} xregs={xregs} {env}")
 
 
+# Batch 1-2 Q4_K: the kernel that streams rows through LDS (the default at
+# batch 1 with K <= 8192) and the register-loading kernel, forced through the
+# planner's override: one super-block per row, more rows than waves, rows of
+# one chunk and of two (16 + 1, 16 + 15 and 16 + 16 super-blocks); the last
+# two shapes take the register-loading kernel either way (batch 2; K > 8192).
+STREAM_CASES = [(1, 256, 1), (5, 1280, 1), (2049, 512, 1), (300, 4352, 1), (77, 7936, 1),
+                (4100, 4096, 1), (4097, 8192, 1), (3, 8192, 2), (33, 8448, 1)]
+
+
+@pytest.mark.parametrize("stream", [0, 1])
+@pytest.mark.parametrize("N,K,B", STREAM_CASES)
+def test_q4_k_dot2_forms(orc, monkeypatch, stream, N, K, B):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_STREAM", str(stream))
+    c = synth.q4_k_case(N, K, B, seed=N + 5 * K + B + stream)
+    announce(f"q4_k gemv N={N} K={K} batch={B} stream={stream}")
+    y = _run_q4_k(c)
+    ref = orc.gemv_q4_k(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"q4_k {N}x{K} b{B} stream={stream}")
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_q4_k_stream_matches_register_kernel(monkeypatch, B):
+    """Both batch-1/2 kernels give lane l units l, l + 64, l + 128, ... of a
+    row, in that order, and reduce the lanes the same way: at K = 8192 their
+    outputs are the same bits."""
+    c = synth.q4_k_case(300, 8192, B, seed=77 + B)
+    W, x = dev(c.W.reshape(-1)), dev(c.x)
+    announce(f"q4_k stream vs register kernel, batch={B}")
+    ys = []
+    for stream in (1, 0):
+        monkeypatch.setenv("LQMM_TUNE_GEMV_STREAM", str(stream))
+        ys.append(host(bq.lqmm_gemv_q4_k(W, x, c.N)))
+    assert np.array_equal(ys[0], ys[1])
+
+
 @pytest.mark.parametrize("name", ["q4_k_gemv_28672x8192_b1", "q4_k_gemv_28672x8192_b8"])
 def test_q4_k_configs(orc, name):
     c = synth.make(name)
