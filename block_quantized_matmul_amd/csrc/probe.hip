@@ -1,9 +1,13 @@
-// Streaming-read probe: the HBM read rate a plain kernel reaches on this GPU,
+// Streaming-read probes: the HBM read rate plain kernels reach on this GPU,
 // reported by the benchmark as context for the GEMV kernels' rates (which are
 // judged against the 8 TB/s datasheet peak). Every 16-byte word of the buffer
-// is read once, grid-stride, with non-temporal loads, eight words in flight
-// per thread. Built as its own library (liblqmm_probe.so); not part of the
-// lqmm interface.
+// is read once, with non-temporal loads, in one of two orders:
+// * grid stride: thread i reads words i, i + G, i + 2G, ... (G = all
+//   threads), eight in flight per thread;
+// * wave blocks: each wave reads whole 4 KB blocks (four 1 KB loads of 64
+//   consecutive 16-byte words), the blocks strided over all waves.
+// Built as its own library (liblqmm_probe.so); not part of the lqmm
+// interface.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,15 +37,46 @@ stream_read_kernel(const u32x4 *__restrict__ p, int64_t n16, uint32_t *out) {
   if (acc == 0x9E3779B9u) out[0] = acc;
 }
 
+constexpr int kBlockLoads = 4;  // 1 KB loads per wave block
+
+__global__ void __launch_bounds__(kThreads)
+block_read_kernel(const u32x4 *__restrict__ p, int64_t n16, uint32_t *out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+  const int64_t nblk = n16 / (kBlockLoads * 64);
+  uint32_t acc = 0;
+  for (int64_t b = wave; b < nblk; b += nw) {
+    const u32x4 *q = p + b * (kBlockLoads * 64) + lane;
+    u32x4 v[kBlockLoads];
+#pragma unroll
+    for (int k = 0; k < kBlockLoads; ++k) v[k] = __builtin_nontemporal_load(q + k * 64);
+#pragma unroll
+    for (int k = 0; k < kBlockLoads; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  // the words after the last whole block
+  for (int64_t i = nblk * (kBlockLoads * 64) + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+       i < n16; i += (int64_t)gridDim.x * kThreads) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) out[0] = acc;
+}
+
 }  // namespace
 
 // Read `bytes` (a multiple of 16) from the 16-byte aligned device buffer p on
-// `stream` with `grid` workgroups of 256 threads; `out` is a device word the
+// `stream` with `grid` workgroups of 256 threads, in grid-stride order
+// (blocks == 0) or in wave blocks (blocks != 0); `out` is a device word the
 // kernel may write. Returns 0, or the HIP error code of the launch.
 extern "C" int lqmm_probe_stream_read(const void *p, int64_t bytes, void *out, int grid,
-                                      void *stream) {
+                                      int blocks, void *stream) {
   if (!p || !out || bytes < 16 || bytes % 16 != 0 || grid < 1) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
-                     static_cast<const u32x4 *>(p), bytes / 16, static_cast<uint32_t *>(out));
+  if (blocks)
+    hipLaunchKernelGGL(block_read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       static_cast<const u32x4 *>(p), bytes / 16, static_cast<uint32_t *>(out));
+  else
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       static_cast<const u32x4 *>(p), bytes / 16, static_cast<uint32_t *>(out));
   return (int)hipGetLastError();
 }
