@@ -151,19 +151,20 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       const int64_t tiles_per_wave = (tiles + grid * (8 / ks) - 1) / (grid * (8 / ks));
       if (env_xregs != 1) xregs = xregs && tiles_per_wave * cps >= 12;
     }
-    // Batch-1 Q4_K with rows of at most 8192 weights streams its rows through
-    // LDS (one workgroup per CU, whole K in one launch, a chunk ring two deep)
-    // when every wave gets at least two rows. Measured: 4% faster at
-    // 28672 x 8192 and 8% at 14336 x 4096, even at 8192 x 8192 (two rows per
-    // wave), 4% slower at 4096 x 4096 (one). Tuning override: 0 off, 1 on
-    // whatever N is, 2 or 3 on with that ring depth.
+    // Batch 1 with rows of at most 8192 weights (Q4_K) or 4096 (Q4_0, two
+    // blocks per unit) streams its rows through LDS (one workgroup per CU, whole K in one
+    // launch, a chunk ring two deep) when every wave gets at least two rows.
+    // Measured on Q4_K: 4% faster at 28672 x 8192 and 8% at 14336 x 4096,
+    // even at 8192 x 8192 (two rows per wave), 4% slower at 4096 x 4096
+    // (one). Tuning override: 0 off, 1 on whatever N is, 2 or 3 on with that
+    // ring depth.
     int streamed = 0;
-    if (fmt == GemvFormat::Q4_K && B == 1 && env_stream != 0 &&
-        units <= lqmm::gemv_stream_max_units()) {
+    if ((f == GemvFormat::Q4_K || f == GemvFormat::Q4_0x2) && B == 1 && env_stream != 0 &&
+        units <= lqmm::gemv_stream_max_units(f)) {
       const int64_t waves_total = (int64_t)num_cus * lqmm::gemv_stream_waves();
       int dr = env_stream == 3 ? 3 : 2;
       if (env_stream >= 1 || N >= 2 * waves_total)
-        streamed = lqmm::gemv_stream_lds_bytes((int)units, dr) <= (size_t)lqmm::kMaxLds ? dr : 0;
+        streamed = lqmm::gemv_stream_lds_bytes(f, (int)units, dr) <= (size_t)lqmm::kMaxLds ? dr : 0;
     }
     // Other MFMA launches: 16-wave workgroups when the staged activations
     // leave room for only one workgroup per CU, so that more loads are in
@@ -213,7 +214,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
       pl.lpr_log2 = lpr_log2;
       pl.lds_bytes = xregs    ? lqmm::gemv_coalr_lds_bytes()
-                     : streamed ? lqmm::gemv_stream_lds_bytes(nu, streamed)
+                     : streamed ? lqmm::gemv_stream_lds_bytes(f, nu, streamed)
                               : lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
       int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
       // The coalesced kernel runs one workgroup per CU: each workgroup stages

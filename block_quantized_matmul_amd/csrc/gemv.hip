@@ -255,6 +255,15 @@ struct FmtQ4_K {
     m = s < 4 ? m_lo : m_hi;
   }
 
+  // Unit uc of a chunk of whole super-blocks copied to LDS at `slot`.
+  static __device__ __forceinline__ Raw read_stream_unit(const u32x4 *slot, int uc) {
+    const u32x4 *sbp = slot + (uc >> 2) * 9;
+    Raw r;
+    r.h = sbp[0];
+    r.q0 = sbp[1 + 2 * (uc & 3)];
+    r.q1 = sbp[2 + 2 * (uc & 3)];
+    return r;
+  }
   // VALU mode. Staged sums per (unit, batch row): (-1024*S_lo, -1024*S_hi),
   // which remove the 1024 bias of each dot product and give the activation
   // sums the dmin * m term needs.
@@ -421,6 +430,16 @@ struct FmtQ4_0x2 {
     uint32_t c;  // bytes 32..35
   };
   static __host__ __device__ __forceinline__ int64_t unit_offset(int64_t unit) { return unit * 36; }
+  // Unit uc of a chunk of whole units copied to LDS at `slot` (36 bytes,
+  // 4-byte aligned: read as dwords).
+  static __device__ __forceinline__ Raw read_stream_unit(const u32x4 *slot, int uc) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(slot) + 9 * uc;
+    Raw r;
+    r.a = u32x4{w[0], w[1], w[2], w[3]};
+    r.b = u32x4{w[4], w[5], w[6], w[7]};
+    r.c = w[8];
+    return r;
+  }
   static __device__ __forceinline__ Raw load(const uint8_t *row, uint32_t unit) {
     const uint8_t *p = row + unit * 36u;
     Raw r;
@@ -450,10 +469,20 @@ struct FmtQ4_0x2 {
   static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
                                                  const float *sums, int u, int nu, bool valid,
                                                  const UnpackMasks &k, float (&acc)[R][B]) {
+    compute_with<B, R>(
+        raw, [&](int b, int t) { return xs[(b * kWords + t) * xstride + u]; },
+        [&](int b, int h) { return sums[2 * (b * nu + u) + h]; }, u, valid, k, acc);
+  }
+  // The same with the unit's staged words and sums taken from xword(b, t)
+  // and sum(b, h) (h: block of the unit), wherever the caller keeps them.
+  template <int B, int R, class XW, class SW>
+  static __device__ __forceinline__ void compute_with(const Raw (&raw)[R], XW xword, SW sum,
+                                                      int /*u*/, bool valid, const UnpackMasks &k,
+                                                      float (&acc)[R][B]) {
     float s[R][B][2];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const float c0 = sums[2 * (b * nu + u)], c1 = sums[2 * (b * nu + u) + 1];
+      const float c0 = sum(b, 0), c1 = sum(b, 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         s[r][b][0] = c0;
@@ -464,7 +493,7 @@ struct FmtQ4_0x2 {
     for (int t = 0; t < kWords; ++t) {
       u32x4 X[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * xstride + u];
+      for (int b = 0; b < B; ++b) X[b] = xword(b, t);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         Nibbles n = unpack_word(word(raw[r], t), k);
@@ -1322,33 +1351,34 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
 }
 
 // ---- VALU mode, weight rows streamed through LDS ------------------------------
-// Batch-1 Q4_K GEMV (K <= 8192) whose weights reach each wave as contiguous
-// chunks: a chunk (16 super-blocks of one row, 2304 bytes) is copied into a
-// wave-private LDS ring slot by buffer-to-LDS loads of 64 x 16 consecutive
-// bytes, with non-temporal hints (every byte is read once), up to DR chunks
-// ahead. Lane l then reads unit l of the chunk from the slot (the
-// super-block header and the unit's two 16-byte quant pieces) and uses the
-// dot2 arithmetic of gemv_kernel. Every load instruction covers 1 KB of one
-// row; gemv_kernel's unit-shaped loads put lanes 32 bytes apart and read
-// each header line from four lanes, which rules out non-temporal loads.
+// Batch-1 GEMV (Q4_K with K <= 8192, or Q4_0 taken two blocks per unit with
+// K <= 4096) whose weights reach each wave as contiguous chunks: a chunk (64
+// units of one row, 2304 bytes: 16 Q4_K super-blocks or 128 Q4_0 blocks) is
+// copied into a wave-private LDS ring slot by buffer-to-LDS loads of 64 x 16
+// consecutive bytes, with non-temporal hints (every byte is read once), up
+// to DR chunks ahead. Lane l then reads unit l of the chunk from the slot
+// (for Q4_K the super-block header and the unit's two 16-byte quant pieces)
+// and uses the dot2 arithmetic of gemv_kernel. Every load instruction covers
+// 1 KB of one row; gemv_kernel's unit-shaped loads put lanes 32 bytes apart
+// and, for Q4_K, read each header line from four lanes, which rules out
+// non-temporal loads.
 // Lane l always takes units l, l + 64, ... of a row (chunk c holds units
 // 64c .. 64c + 63), so after the workgroup has staged x it keeps the staged
 // words and sums of its first unit in registers: for rows of up to 4096
-// weights the LDS then serves only the weight chunks. Sixteen waves per workgroup, one workgroup per CU; waves
-// take whole rows, row r by wave r mod (waves in the grid). The first chunks
-// are requested before the staging (the ring does not overlap the staged
-// activations), and a chunk's units are read from LDS during the previous
-// chunk's arithmetic.
+// weights the LDS then serves only the weight chunks. Sixteen waves per
+// workgroup, one workgroup per CU; waves take whole rows, row r by wave
+// r mod (waves in the grid). The first chunks are requested before the
+// staging (the ring does not overlap the staged activations), and a chunk's
+// units are read from LDS during the previous chunk's arithmetic.
 // Waits: as in gemv_coalr_kernel (loads return in order; a slot is refilled
 // only after the wave's reads of it are complete; chunks past the wave's
 // work come from an empty buffer range).
 constexpr int kStreamWaves = 16;
 constexpr int kStreamThreads = kStreamWaves * kWave;
-constexpr int kStreamChunkSB = 16;                 // super-blocks per chunk (144 B each)
-constexpr int kStreamSlot = kStreamChunkSB * 144;  // 2304 bytes
+constexpr int kStreamUnitBytes = 36;                // a Q4_K quarter super-block or two Q4_0 blocks
+constexpr int kStreamSlot = kWave * kStreamUnitBytes;  // a chunk: 64 units, 2304 bytes
 constexpr int kStreamLoads = (kStreamSlot + kWave * 16 - 1) / (kWave * 16);  // 3 (the last 256 B)
 constexpr int kStreamMaxUPL = 2;                   // chunks (units per lane) per row: K <= 8192
-static_assert(kStreamChunkSB * 4 == kWave, "one unit per lane");
 
 template <class F>
 __host__ __device__ __forceinline__ size_t stream_stage_bytes(int nu) {
@@ -1372,13 +1402,11 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   uint8_t *const ring = smem + stream_stage_bytes<F>(nu) + (size_t)wave * DR * kStreamSlot;
-  const int nsb = nu / 4;  // super-blocks per row: UPL - 1 full chunks and a last one
   const int64_t nwaves = (int64_t)gridDim.x * kStreamWaves;
   const int64_t wave_id = (int64_t)blockIdx.x * kStreamWaves + wave;
   const int64_t n_rows = wave_id < N ? (N - wave_id + nwaves - 1) / nwaves : 0;
-  auto chunk_units = [&](int c) {  // units in chunk c of a row
-    return 4 * (nsb - c * kStreamChunkSB < kStreamChunkSB ? nsb - c * kStreamChunkSB
-                                                          : kStreamChunkSB);
+  auto chunk_units = [&](int c) {  // units in chunk c of a row: UPL - 1 full chunks, a last one
+    return nu - c * kWave < kWave ? nu - c * kWave : kWave;
   };
 
   // Request item `issued` (chunk ic of row irow) into ring slot `slot`.
@@ -1387,15 +1415,16 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   auto issue = [&](int slot) {
     const bool live = issued < n_rows * UPL;
     const int64_t r = irow < N ? irow : N - 1;
-    const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * (kStreamChunkSB * 144),
-                                live ? (uint32_t)(chunk_units(ic) * 36) : 0u);
+    const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * kStreamSlot,
+                                live ? (uint32_t)(chunk_units(ic) * kStreamUnitBytes) : 0u);
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       // the last load covers the slot's tail only: its other lanes are
       // switched off, so that nothing is written past the slot
       if ((k + 1) * kWave * 16 <= kStreamSlot || lane * 16 < kStreamSlot - k * kWave * 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring + slot * kStreamSlot + k * (kWave * 16),
-                                                 16, k * (kWave * 16) + lane * 16, 0, 0, 2 /* nt */);
+                                                 16, k * (kWave * 16) + lane * 16, 0, 0,
+                                                 2 /* non-temporal */);
     }
     ++issued;
     if (++ic == UPL) {
@@ -1437,12 +1466,8 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
 
   // Lane's unit of the chunk in `slot` (clamped into the chunk).
   auto read_unit = [&](int slot, int nuc, typename F::Raw &r) {
-    const u32x4 *wb = reinterpret_cast<const u32x4 *>(ring + slot * kStreamSlot);
-    const int uc = lane < nuc ? lane : nuc - 1;
-    const u32x4 *sbp = wb + (uc >> 2) * 9;
-    r.h = sbp[0];
-    r.q0 = sbp[1 + 2 * (uc & 3)];
-    r.q1 = sbp[2 + 2 * (uc & 3)];
+    r = F::read_stream_unit(reinterpret_cast<const u32x4 *>(ring + slot * kStreamSlot),
+                            lane < nuc ? lane : nuc - 1);
   };
 
   // The next chunk's unit is read early (during this chunk's arithmetic).
@@ -1687,15 +1712,20 @@ hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, floa
   } else {
     if (pl.mfma) return launch_fmt_mfma<F>(pl, W, x, y, s);
   }
-  if constexpr (std::is_same<F, FmtQ4_K>::value) {
+  if constexpr (std::is_same<F, FmtQ4_K>::value || std::is_same<F, FmtQ4_0x2>::value) {
     if (pl.stream) {
       // batch 1, the whole row in one launch, at most kStreamMaxUPL chunks
-      const int upl = (pl.nu / 4 + kStreamChunkSB - 1) / kStreamChunkSB;
+      const int upl = (pl.nu + kWave - 1) / kWave;
       if (pl.batch != 1 || pl.unit0 != 0 || pl.accumulate || upl > kStreamMaxUPL)
         return hipErrorInvalidValue;
-      if (pl.stream == 3)
-        return upl == 1 ? launch_stream<F, 1, 3>(pl, W, x, y, s) : launch_stream<F, 2, 3>(pl, W, x, y, s);
-      return upl == 1 ? launch_stream<F, 1, 2>(pl, W, x, y, s) : launch_stream<F, 2, 2>(pl, W, x, y, s);
+      if (upl == 1)
+        return pl.stream == 3 ? launch_stream<F, 1, 3>(pl, W, x, y, s)
+                              : launch_stream<F, 1, 2>(pl, W, x, y, s);
+      // two chunks per row: Q4_K only (the Q4_0 pair form spills there)
+      if constexpr (std::is_same<F, FmtQ4_K>::value)
+        return pl.stream == 3 ? launch_stream<F, 2, 3>(pl, W, x, y, s)
+                              : launch_stream<F, 2, 2>(pl, W, x, y, s);
+      return hipErrorInvalidValue;
     }
   }
   const bool full = pl.lpr_log2 == 6;
@@ -1734,11 +1764,15 @@ size_t gemv_coalr_lds_bytes() {
   return (size_t)kWavesPerWg * kCoalrRing * 3 * kWave * 16 + (size_t)2 * kWavesPerWg * kWave * 16;
 }
 
-size_t gemv_stream_lds_bytes(int nu, int depth) {
-  return stream_stage_bytes<FmtQ4_K>(nu) + (size_t)kStreamWaves * depth * kStreamSlot;
+size_t gemv_stream_lds_bytes(GemvFormat f, int nu, int depth) {
+  const size_t stage = f == GemvFormat::Q4_K ? stream_stage_bytes<FmtQ4_K>(nu)
+                                             : stream_stage_bytes<FmtQ4_0x2>(nu);
+  return stage + (size_t)kStreamWaves * depth * kStreamSlot;
 }
 
-int gemv_stream_max_units() { return kStreamMaxUPL * kStreamChunkSB * 4; }
+int gemv_stream_max_units(GemvFormat f) {
+  return (f == GemvFormat::Q4_K ? kStreamMaxUPL : 1) * kWave;
+}
 
 int gemv_stream_waves() { return kStreamWaves; }
 

@@ -227,19 +227,41 @@ def test_q4_k_dot2_forms(orc, monkeypatch, stream, N, K, B):
     assert_close(y, ref, TOL_QUANT, f"q4_k {N}x{K} b{B} stream={stream}")
 
 
-@pytest.mark.parametrize("B", [1, 2])
-def test_q4_k_stream_matches_register_kernel(monkeypatch, B):
-    """Both batch-1/2 kernels give lane l units l, l + 64, l + 128, ... of a
-    row, in that order, and reduce the lanes the same way: at K = 8192 their
-    outputs are the same bits."""
-    c = synth.q4_k_case(300, 8192, B, seed=77 + B)
+@pytest.mark.parametrize("fmt,K", [("q4_k", 8192), ("q4_0", 4096)])
+def test_stream_matches_register_kernel(monkeypatch, fmt, K):
+    """Both batch-1 kernels give lane l units l, l + 64, ... of a row, in
+    that order, and reduce the lanes the same way: their outputs are the same
+    bits (Q4_0 in two-block units)."""
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(300, K, 1, seed=77 + K)
     W, x = dev(c.W.reshape(-1)), dev(c.x)
-    announce(f"q4_k stream vs register kernel, batch={B}")
+    call = bq.lqmm_gemv_q4_k if fmt == "q4_k" else bq.lqmm_gemv_q4_0
+    monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", "1")
+    announce(f"{fmt} stream vs register kernel, K={K}")
     ys = []
     for stream in (1, 0):
         monkeypatch.setenv("LQMM_TUNE_GEMV_STREAM", str(stream))
-        ys.append(host(bq.lqmm_gemv_q4_k(W, x, c.N)))
+        ys.append(host(call(W, x, c.N)))
     assert np.array_equal(ys[0], ys[1])
+
+
+# Batch-1 Q4_0 in two-block units: streamed (forced) and register-loading;
+# K = 4160 (rows over one chunk) and K = 4128 (K % 64 != 0, single-block
+# units) take the register-loading kernel either way.
+Q4_0_STREAM_CASES = [(1, 64, 1), (300, 2048, 1), (8193, 1024, 1), (9000, 4096, 1), (77, 4160, 1),
+                     (40, 4128, 1)]
+
+
+@pytest.mark.parametrize("stream", [0, 1])
+@pytest.mark.parametrize("N,K,B", Q4_0_STREAM_CASES)
+def test_q4_0_dot2_forms(orc, monkeypatch, stream, N, K, B):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_STREAM", str(stream))
+    monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", "1")
+    c = synth.q4_0_case(N, K, B, seed=N + 7 * K + stream)
+    announce(f"q4_0 gemv N={N} K={K} batch={B} stream={stream}")
+    y = _run_q4_0(c)
+    ref = orc.gemv_q4_0(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"q4_0 {N}x{K} b{B} stream={stream}")
 
 
 @pytest.mark.parametrize("name", ["q4_k_gemv_28672x8192_b1", "q4_k_gemv_28672x8192_b8"])
