@@ -77,6 +77,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   const int env_pair = env_int("LQMM_TUNE_GEMV_Q4_0_PAIR");
   const int env_xregs = env_int("LQMM_TUNE_GEMV_XREGS");
   const int env_stream = env_int("LQMM_TUNE_GEMV_STREAM");
+  const int env_stream_batch = env_int("LQMM_TUNE_GEMV_STREAM_BATCH");
   const int64_t tiles = (N + 15) / 16;  // 16-row tiles of the matrix-core kernels
 
   // K-slices per tile of the coalesced kernel (one workgroup per CU): the
@@ -114,16 +115,40 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     // not grow with the batch, the dot2 path's does.
     bool mfma = left >= 3;
     if (env_mfma == 0 || env_mfma == 1) mfma = env_mfma == 1;
-    const int bmax = mfma ? 16 : 2;
-    const int B = (int)(left < bmax ? left : bmax);
     // VALU-mode Q4_0 takes two blocks per unit when K % 64 == 0: 36-byte,
     // 4-byte-aligned loads instead of an 18-byte block per lane. Measured:
     // faster when there are more rows than one workgroup per CU covers (a
     // wave per two rows), slower with only one workgroup per CU.
     const int64_t rows_one_wg_per_cu = (int64_t)num_cus * waves_per_wg * 2;
-    bool pair = fmt == GemvFormat::Q4_0 && !mfma && K % 64 == 0 && N > rows_one_wg_per_cu;
-    if (env_pair == 0 || env_pair == 1) pair = fmt == GemvFormat::Q4_0 && !mfma && K % 64 == 0 && env_pair == 1;
-    const GemvFormat f = pair ? GemvFormat::Q4_0x2 : fmt;
+    auto pair_for = [&](bool valu) {
+      if (env_pair == 0 || env_pair == 1)
+        return fmt == GemvFormat::Q4_0 && valu && K % 64 == 0 && env_pair == 1;
+      return fmt == GemvFormat::Q4_0 && valu && K % 64 == 0 && N > rows_one_wg_per_cu;
+    };
+    // The kernel that streams rows through LDS (one workgroup per CU, whole
+    // K in one launch) takes rows of at most 8192 weights (Q4_K) or 4096
+    // (Q4_0, two blocks per unit) at up to two activation rows (the second
+    // row reads its activations from LDS), when every wave gets at least two
+    // weight rows. Measured on Q4_K at batch 1: 4% faster at 28672 x 8192
+    // and 8% at 14336 x 4096, even at 8192 x 8192 (two rows per wave), 4%
+    // slower at 4096 x 4096 (one); at batch 2 4-5% faster (Q4_K 28672 x
+    // 8192, Q4_0 12288 x 4096). Overrides: LQMM_TUNE_GEMV_STREAM 0 off, 1 on
+    // whatever N is; LQMM_TUNE_GEMV_STREAM_BATCH 1 or 2.
+    const int64_t stream_waves_total = (int64_t)num_cus * lqmm::gemv_stream_waves();
+    const GemvFormat fs = pair_for(true) ? GemvFormat::Q4_0x2 : fmt;
+    int stream_batch = lqmm::gemv_stream_max_batch();
+    if (env_stream_batch >= 1 && env_stream_batch <= lqmm::gemv_stream_max_batch())
+      stream_batch = env_stream_batch;
+    const int64_t units_s = K / lqmm::gemv_unit_weights(fs);
+    const bool streamed =
+        (fs == GemvFormat::Q4_K || fs == GemvFormat::Q4_0x2) && env_stream != 0 && env_mfma != 1 &&
+        left <= stream_batch && units_s <= lqmm::gemv_stream_max_units(fs) &&
+        (env_stream == 1 || N >= 2 * stream_waves_total) &&
+        lqmm::gemv_stream_lds_bytes(fs, (int)left, (int)units_s) <= (size_t)lqmm::kMaxLds;
+    if (streamed) mfma = false;
+    const int bmax = mfma ? 16 : streamed ? stream_batch : 2;
+    const int B = (int)(left < bmax ? left : bmax);
+    const GemvFormat f = streamed ? fs : pair_for(!mfma) ? GemvFormat::Q4_0x2 : fmt;
     const int uw = lqmm::gemv_unit_weights(f);
     const int64_t units = K / uw;
     // MFMA mode uses the coalesced kernel (loads staged through LDS, 8
@@ -150,21 +175,6 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       const int64_t grid = wgs < (int64_t)num_cus ? wgs : (int64_t)num_cus;
       const int64_t tiles_per_wave = (tiles + grid * (8 / ks) - 1) / (grid * (8 / ks));
       if (env_xregs != 1) xregs = xregs && tiles_per_wave * cps >= 12;
-    }
-    // Batch 1 with rows of at most 8192 weights (Q4_K) or 4096 (Q4_0, two
-    // blocks per unit) streams its rows through LDS (one workgroup per CU, whole K in one
-    // launch, a chunk ring two deep) when every wave gets at least two rows.
-    // Measured on Q4_K: 4% faster at 28672 x 8192 and 8% at 14336 x 4096,
-    // even at 8192 x 8192 (two rows per wave), 4% slower at 4096 x 4096
-    // (one). Tuning override: 0 off, 1 on whatever N is, 2 or 3 on with that
-    // ring depth.
-    int streamed = 0;
-    if ((f == GemvFormat::Q4_K || f == GemvFormat::Q4_0x2) && B == 1 && env_stream != 0 &&
-        units <= lqmm::gemv_stream_max_units(f)) {
-      const int64_t waves_total = (int64_t)num_cus * lqmm::gemv_stream_waves();
-      int dr = env_stream == 3 ? 3 : 2;
-      if (env_stream >= 1 || N >= 2 * waves_total)
-        streamed = lqmm::gemv_stream_lds_bytes(f, (int)units, dr) <= (size_t)lqmm::kMaxLds ? dr : 0;
     }
     // Other MFMA launches: 16-wave workgroups when the staged activations
     // leave room for only one workgroup per CU, so that more loads are in
@@ -214,7 +224,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
       while ((1 << lpr_log2) < nu && lpr_log2 < 6) ++lpr_log2;
       pl.lpr_log2 = lpr_log2;
       pl.lds_bytes = xregs    ? lqmm::gemv_coalr_lds_bytes()
-                     : streamed ? lqmm::gemv_stream_lds_bytes(f, nu, streamed)
+                     : streamed ? lqmm::gemv_stream_lds_bytes(f, B, nu)
                               : lqmm::gemv_lds_bytes(f, mfma, B, nu) + red_bytes;
       int64_t wg_per_cu = (int64_t)(160 * 1024) / (int64_t)(pl.lds_bytes ? pl.lds_bytes : 1);
       // The coalesced kernel runs one workgroup per CU: each workgroup stages

@@ -1379,33 +1379,46 @@ constexpr int kStreamUnitBytes = 36;                // a Q4_K quarter super-bloc
 constexpr int kStreamSlot = kWave * kStreamUnitBytes;  // a chunk: 64 units, 2304 bytes
 constexpr int kStreamLoads = (kStreamSlot + kWave * 16 - 1) / (kWave * 16);  // 3 (the last 256 B)
 constexpr int kStreamMaxUPL = 2;                   // chunks (units per lane) per row: K <= 8192
+constexpr int kStreamDepth = 2;  // ring slots per wave (measured: faster than 3 at every shape tried)
+// Activation rows per launch. Measured on Q4_K 28672 x 8192: 2 rows 33.1 ->
+// 31.4 us against gemv_kernel, but 3 and 4 rows 37.5 and 43.2 us against
+// 29.8 and 30.6 us on the matrix cores (the dot2 work grows with the rows).
+constexpr int kStreamMaxBatch = 2;
 
 template <class F>
-__host__ __device__ __forceinline__ size_t stream_stage_bytes(int nu) {
-  const size_t b = (size_t)F::kWords * staged_stride<F>(nu) * 16 + (size_t)nu * F::kSums * 4;
+__host__ __device__ __forceinline__ size_t stream_stage_bytes(int batch, int nu) {
+  const size_t b = (size_t)batch * F::kWords * staged_stride<F>(nu) * 16 +
+                   (size_t)batch * nu * F::kSums * 4;
   return (b + 15) & ~(size_t)15;
 }
 
-template <class F, int UPL, int DR>
+template <class F, int B, int DR>
 __global__ void __launch_bounds__(kStreamThreads)
 gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
-                   const float *__restrict__ x, float *__restrict__ y, int64_t N) {
+                   const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int64_t ldy,
+                   int64_t N) {
   constexpr int T = F::kWords;
   constexpr int NI = kStreamLoads;
   static_assert((DR - 1) * NI <= 63, "load counter range");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot t*NS + u
+  u32x4 *xs = reinterpret_cast<u32x4 *>(smem);  // slot (b*T + t)*NS + u
   const int NS = staged_stride<F>(nu);
-  float *sums = reinterpret_cast<float *>(smem + (size_t)T * NS * 16);
+  float *sums = reinterpret_cast<float *>(smem + (size_t)B * T * NS * 16);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  uint8_t *const ring = smem + stream_stage_bytes<F>(nu) + (size_t)wave * DR * kStreamSlot;
+  uint8_t *const ring = smem + stream_stage_bytes<F>(B, nu) + (size_t)wave * DR * kStreamSlot;
   const int64_t nwaves = (int64_t)gridDim.x * kStreamWaves;
   const int64_t wave_id = (int64_t)blockIdx.x * kStreamWaves + wave;
   const int64_t n_rows = wave_id < N ? (N - wave_id + nwaves - 1) / nwaves : 0;
-  auto chunk_units = [&](int c) {  // units in chunk c of a row: UPL - 1 full chunks, a last one
+  // Chunks per row: Q4_K 1 or 2, kept a run-time value, so that the chunk
+  // loop below stays a loop (the compiler keeps it within 128 VGPRs); the
+  // Q4_0 pair form takes one chunk per row (with a second one it spilled).
+  constexpr bool kOneChunk = std::is_same<F, FmtQ4_0x2>::value;
+  static_assert(B <= kStreamMaxBatch, "activation rows");
+  const int cpr = kOneChunk ? 1 : (nu + kWave - 1) / kWave;
+  auto chunk_units = [&](int c) {  // units in chunk c of a row: cpr - 1 full chunks, a last one
     return nu - c * kWave < kWave ? nu - c * kWave : kWave;
   };
 
@@ -1413,7 +1426,7 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   int64_t irow = wave_id, issued = 0;
   int ic = 0;
   auto issue = [&](int slot) {
-    const bool live = issued < n_rows * UPL;
+    const bool live = issued < n_rows * cpr;
     const int64_t r = irow < N ? irow : N - 1;
     const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * kStreamSlot,
                                 live ? (uint32_t)(chunk_units(ic) * kStreamUnitBytes) : 0u);
@@ -1427,7 +1440,7 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
                                                  2 /* non-temporal */);
     }
     ++issued;
-    if (++ic == UPL) {
+    if (++ic == cpr) {
       ic = 0;
       irow += nwaves;
     }
@@ -1435,28 +1448,31 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
 #pragma unroll
   for (int k = 0; k < DR; ++k) issue(k);
 
-  // Stage the activation words, then the per-unit sums, as gemv_kernel does;
-  // then each lane copies those of its units into registers. The barriers
-  // wait for LDS operations only, not for the chunk requests above.
-  stage_words<F, kStreamThreads, 1>(xs, 1, nu, x, nu * F::kUnitWeights, 0.0625f,
-                                    [&](int, int u, int t) { return t * NS + u; });
+  // Stage the activation words, then the per-(b, u) sums, as gemv_kernel
+  // does; at batch 1 each lane then copies those of its first unit into
+  // registers. The barriers wait for LDS operations only, not for the chunk
+  // requests above.
+  stage_words<F, kStreamThreads, 1>(xs, B, nu, x, ldx, 0.0625f,
+                                    [&](int b, int u, int t) { return (b * T + t) * NS + u; });
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int u = tid; u < nu; u += kStreamThreads) {
+  for (int i = tid; i < B * nu; i += kStreamThreads) {
+    const int u = i % nu, b = i / nu;
 #pragma unroll
     for (int g = 0; g < T / F::kSumWords; ++g) {
       float slo = 0.0f, shi = 0.0f;
 #pragma unroll
       for (int t = g * F::kSumWords; t < (g + 1) * F::kSumWords; ++t)
-        word_sums(xs[t * NS + u], slo, shi);
-      F::stage_sums(sums, u, g, slo, shi);
+        word_sums(xs[(b * T + t) * NS + u], slo, shi);
+      F::stage_sums(sums, i, g, slo, shi);
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  // Registers hold the first chunk's activations; those of a second chunk
-  // stay in LDS (there are no registers left for them).
-  u32x4 xr[T];
+  // At batch 1, registers hold the first chunk's activations; those of a
+  // second chunk, and all of them at larger batches, stay in LDS (there are
+  // no registers left for them).
+  u32x4 xr[B == 1 ? T : 1];
   float sr[2];
-  {
+  if (B == 1) {
     const int u = lane < nu ? lane : nu - 1;
 #pragma unroll
     for (int t = 0; t < T; ++t) xr[t] = xs[t * NS + u];
@@ -1470,48 +1486,44 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
                             lane < nuc ? lane : nuc - 1);
   };
 
-  // The next chunk's unit is read early (during this chunk's arithmetic).
-  constexpr bool kEarly = true;
   const UnpackMasks kmask;
   int slot = 0;
+  // the next chunk's unit is read during this chunk's arithmetic
   typename F::Raw nx[1];
-  if (kEarly) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
-    read_unit(0, chunk_units(0), nx[0]);
-  }
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+  read_unit(0, chunk_units(0), nx[0]);
   int64_t crow = wave_id;
   for (int64_t rr = 0; rr < n_rows; ++rr) {
-    float acc[1][1] = {{0.0f}};
+    float acc[1][B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[0][b] = 0.0f;
 #pragma nounroll
-    for (int c = 0; c < UPL; ++c) {
+    for (int c = 0; c < cpr; ++c) {
       __builtin_amdgcn_sched_barrier(0);
-      typename F::Raw rw[1];
-      if (kEarly) {
-        rw[0] = nx[0];
-      } else {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
-        read_unit(slot, chunk_units(c), rw[0]);
-      }
+      typename F::Raw rw[1] = {nx[0]};
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       issue(slot);
       slot = slot + 1 == DR ? 0 : slot + 1;
-      if (kEarly) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
-        // past the wave's last chunk this reads a slot of zeros: harmless
-        read_unit(slot, chunk_units(0), nx[0]);
-      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
+      // past the wave's last chunk this reads a slot of zeros: harmless
+      read_unit(slot, chunk_units(0), nx[0]);
       const int nuc = chunk_units(c);
       const bool valid = lane < nuc;
       const int u = c * kWave + (valid ? lane : 0);
-      if (c == 0)
-        F::template compute_with<1, 1>(
-            rw, [&](int, int t) { return xr[t]; }, [&](int, int h) { return sr[h]; }, u, valid,
-            kmask, acc);
+      if (B == 1 && c == 0)
+        F::template compute_with<B, 1>(
+            rw, [&](int, int t) { return xr[B == 1 ? t : 0]; }, [&](int, int h) { return sr[h]; },
+            u, valid, kmask, acc);
       else
-        F::template compute<1, 1>(rw, xs, NS, sums, u, nu, valid, kmask, acc);
+        F::template compute_with<B, 1>(
+            rw, [&](int b, int t) { return xs[(b * T + t) * NS + u]; },
+            [&](int b, int h) { return sums[2 * (b * nu + u) + h]; }, u, valid, kmask, acc);
     }
-    const float v = group_sum(acc[0][0], kWave);
-    if (lane == kWave - 1) y[crow] = v;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = group_sum(acc[0][b], kWave);
+      if (lane == kWave - 1) y[b * ldy + crow] = v;
+    }
     crow += nwaves;
   }
   // no buffer-to-LDS load may be left in flight when the wave ends
@@ -1524,10 +1536,10 @@ hipError_t set_lds_attr(K kern) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxGemvLds);
 }
 
-template <class F, int UPL, int DR>
+template <class F, int B, int DR>
 hipError_t launch_stream(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                          hipStream_t stream) {
-  auto kern = gemv_stream_kernel<F, UPL, DR>;
+  auto kern = gemv_stream_kernel<F, B, DR>;
   static bool attr_done = false;  // benign race: setting the attribute twice is harmless
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1536,8 +1548,16 @@ hipError_t launch_stream(const GemvPlan &pl, const uint8_t *W, const float *x, f
     attr_done = true;
   }
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kStreamThreads), pl.lds_bytes, stream, W,
-                     pl.row_bytes, pl.nu, x, y, pl.N);
+                     pl.row_bytes, pl.nu, x, pl.ldx, y, pl.ldy, pl.N);
   return hipGetLastError();
+}
+
+template <class F>
+hipError_t launch_stream_b(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
+                           hipStream_t s) {
+  if (pl.batch == 1) return launch_stream<F, 1, kStreamDepth>(pl, W, x, y, s);
+  if (pl.batch == 2) return launch_stream<F, 2, kStreamDepth>(pl, W, x, y, s);
+  return hipErrorInvalidValue;
 }
 
 template <class F, int B, int R, int U, bool FULL>
@@ -1714,18 +1734,10 @@ hipError_t launch_fmt(const GemvPlan &pl, const uint8_t *W, const float *x, floa
   }
   if constexpr (std::is_same<F, FmtQ4_K>::value || std::is_same<F, FmtQ4_0x2>::value) {
     if (pl.stream) {
-      // batch 1, the whole row in one launch, at most kStreamMaxUPL chunks
+      // the whole row in one launch, at most kStreamMaxUPL chunks
       const int upl = (pl.nu + kWave - 1) / kWave;
-      if (pl.batch != 1 || pl.unit0 != 0 || pl.accumulate || upl > kStreamMaxUPL)
-        return hipErrorInvalidValue;
-      if (upl == 1)
-        return pl.stream == 3 ? launch_stream<F, 1, 3>(pl, W, x, y, s)
-                              : launch_stream<F, 1, 2>(pl, W, x, y, s);
-      // two chunks per row: Q4_K only (the Q4_0 pair form spills there)
-      if constexpr (std::is_same<F, FmtQ4_K>::value)
-        return pl.stream == 3 ? launch_stream<F, 2, 3>(pl, W, x, y, s)
-                              : launch_stream<F, 2, 2>(pl, W, x, y, s);
-      return hipErrorInvalidValue;
+      if (pl.unit0 != 0 || pl.accumulate || upl > kStreamMaxUPL) return hipErrorInvalidValue;
+      return launch_stream_b<F>(pl, W, x, y, s);
     }
   }
   const bool full = pl.lpr_log2 == 6;
@@ -1764,11 +1776,13 @@ size_t gemv_coalr_lds_bytes() {
   return (size_t)kWavesPerWg * kCoalrRing * 3 * kWave * 16 + (size_t)2 * kWavesPerWg * kWave * 16;
 }
 
-size_t gemv_stream_lds_bytes(GemvFormat f, int nu, int depth) {
-  const size_t stage = f == GemvFormat::Q4_K ? stream_stage_bytes<FmtQ4_K>(nu)
-                                             : stream_stage_bytes<FmtQ4_0x2>(nu);
-  return stage + (size_t)kStreamWaves * depth * kStreamSlot;
+size_t gemv_stream_lds_bytes(GemvFormat f, int batch, int nu) {
+  const size_t stage = f == GemvFormat::Q4_K ? stream_stage_bytes<FmtQ4_K>(batch, nu)
+                                             : stream_stage_bytes<FmtQ4_0x2>(batch, nu);
+  return stage + (size_t)kStreamWaves * kStreamDepth * kStreamSlot;
 }
+
+int gemv_stream_max_batch() { return kStreamMaxBatch; }
 
 int gemv_stream_max_units(GemvFormat f) {
   return (f == GemvFormat::Q4_K ? kStreamMaxUPL : 1) * kWave;

@@ -28,8 +28,8 @@ struct GemvPlan {
   int depth;          // lds_stage: chunks in flight per wave (2, 3, 4 or 6)
   int xregs;          // lds_stage: activations in registers (whole K in one launch, U = 1)
   int cps;            // xregs: super-chunks per k-slice (1..4)
-  int stream;         // VALU mode, batch 1, Q4_K or Q4_0x2: 0, or the chunk ring depth (2 or 3)
-                      // of the kernel that streams rows through LDS (whole K in one launch)
+  int stream;         // VALU mode, Q4_K or Q4_0x2: the kernel that streams rows through LDS
+                      // (batch 1 or 2, whole K in one launch)
   int lpr_log2;       // log2(lanes sharing one weight row)
   int nu;             // units (of gemv_unit_weights weights) per row in this launch
   int64_t unit0;      // first unit of each row covered by this launch
@@ -45,7 +45,8 @@ size_t gemv_lds_bytes(GemvFormat f, bool mfma, int batch, int nu);
 size_t gemv_mfma_reduce_bytes(int waves);  // extra LDS of an MFMA-mode launch
 size_t gemv_coal_stage_bytes(int u);        // per-workgroup staging of the coalesced MFMA kernel
 size_t gemv_coalr_lds_bytes();              // LDS of the coalesced kernel with activations in registers
-size_t gemv_stream_lds_bytes(GemvFormat f, int nu, int depth);  // LDS of the streamed batch-1 kernel
+size_t gemv_stream_lds_bytes(GemvFormat f, int batch, int nu);  // LDS of the streamed kernel
+int gemv_stream_max_batch();                      // the most activation rows it takes
 int gemv_stream_waves();                          // its waves per workgroup
 int gemv_stream_max_units(GemvFormat f);          // the longest row it takes, in 64-weight units
 // whether a k-slice of cps super-chunks of `batch` activation rows can be

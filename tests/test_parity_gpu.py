@@ -208,12 +208,13 @@ def test_coal_forms(orc, monkeypatch, xregs, fmt, N, K, B, env):
 
 
 # Batch 1-2 Q4_K: the kernel that streams rows through LDS (the default at
-# batch 1 with K <= 8192) and the register-loading kernel, forced through the
-# planner's override: one super-block per row, more rows than waves, rows of
-# one chunk and of two (16 + 1, 16 + 15 and 16 + 16 super-blocks); the last
-# two shapes take the register-loading kernel either way (batch 2; K > 8192).
-STREAM_CASES = [(1, 256, 1), (5, 1280, 1), (2049, 512, 1), (300, 4352, 1), (77, 7936, 1),
-                (4100, 4096, 1), (4097, 8192, 1), (3, 8192, 2), (33, 8448, 1)]
+# K <= 8192 with two weight rows per wave or more) and the register-loading
+# kernel, forced through the planner's override: one super-block per row,
+# more rows than waves, rows of one chunk and of two (16 + 1, 16 + 15 and
+# 16 + 16 super-blocks), one and two activation rows; the last shape takes
+# the register-loading kernel either way (K > 8192).
+STREAM_CASES = [(1, 256, 1), (5, 1280, 2), (2049, 512, 1), (300, 4352, 1), (77, 7936, 2),
+                (4100, 4096, 1), (4097, 8192, 1), (3, 8192, 2), (300, 8192, 2), (33, 8448, 1)]
 
 
 @pytest.mark.parametrize("stream", [0, 1])
@@ -227,13 +228,14 @@ def test_q4_k_dot2_forms(orc, monkeypatch, stream, N, K, B):
     assert_close(y, ref, TOL_QUANT, f"q4_k {N}x{K} b{B} stream={stream}")
 
 
+@pytest.mark.parametrize("B", [1, 2])
 @pytest.mark.parametrize("fmt,K", [("q4_k", 8192), ("q4_0", 4096)])
-def test_stream_matches_register_kernel(monkeypatch, fmt, K):
-    """Both batch-1 kernels give lane l units l, l + 64, ... of a row, in
+def test_stream_matches_register_kernel(monkeypatch, fmt, K, B):
+    """Both batch-1/2 kernels give lane l units l, l + 64, ... of a row, in
     that order, and reduce the lanes the same way: their outputs are the same
     bits (Q4_0 in two-block units)."""
     make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
-    c = make(300, K, 1, seed=77 + K)
+    c = make(300, K, B, seed=77 + K + B)
     W, x = dev(c.W.reshape(-1)), dev(c.x)
     call = bq.lqmm_gemv_q4_k if fmt == "q4_k" else bq.lqmm_gemv_q4_0
     monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", "1")
@@ -245,11 +247,11 @@ def test_stream_matches_register_kernel(monkeypatch, fmt, K):
     assert np.array_equal(ys[0], ys[1])
 
 
-# Batch-1 Q4_0 in two-block units: streamed (forced) and register-loading;
+# Batch 1-2 Q4_0 in two-block units: streamed (forced) and register-loading;
 # K = 4160 (rows over one chunk) and K = 4128 (K % 64 != 0, single-block
 # units) take the register-loading kernel either way.
 Q4_0_STREAM_CASES = [(1, 64, 1), (300, 2048, 1), (8193, 1024, 1), (9000, 4096, 1), (77, 4160, 1),
-                     (40, 4128, 1)]
+                     (40, 4128, 1), (300, 4096, 2), (8193, 2048, 2)]
 
 
 @pytest.mark.parametrize("stream", [0, 1])
