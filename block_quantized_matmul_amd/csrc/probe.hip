@@ -1,6 +1,6 @@
 // Streaming-read probes: the HBM read rate plain kernels reach on this GPU,
 // reported by the benchmark as context for the GEMV kernels' rates (which are
-// judged against the 8 TB/s datasheet peak). Every 16-byte word of the buffer
+// stated against the 8 TB/s datasheet peak). Every 16-byte word of the buffer
 // is read once, with non-temporal loads, in one of two orders:
 // * grid stride: thread i reads words i, i + G, i + 2G, ... (G = all
 //   threads), eight in flight per thread;
