@@ -1506,7 +1506,7 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
       slot = slot + 1 == DR ? 0 : slot + 1;
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DR - 1) * NI) : "memory");
       // past the wave's last chunk this reads a slot of zeros: harmless
-      read_unit(slot, chunk_units(0), nx[0]);
+      read_unit(slot, chunk_units(c + 1 == cpr ? 0 : c + 1), nx[0]);
       const int nuc = chunk_units(c);
       const bool valid = lane < nuc;
       const int u = c * kWave + (valid ? lane : 0);
