@@ -1376,8 +1376,14 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
 constexpr int kStreamWaves = 16;
 constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kStreamUnitBytes = 36;                // a Q4_K quarter super-block or two Q4_0 blocks
-constexpr int kStreamSlot = kWave * kStreamUnitBytes;  // a chunk: 64 units, 2304 bytes
-constexpr int kStreamLoads = (kStreamSlot + kWave * 16 - 1) / (kWave * 16);  // 3 (the last 256 B)
+constexpr int kStreamChunk = kWave * kStreamUnitBytes;  // a chunk: 64 units, 2304 bytes
+constexpr int kStreamLoads = (kStreamChunk + kWave * 16 - 1) / (kWave * 16);  // 3
+// A ring slot holds whole loads (3 KB): the last load's lanes past the chunk
+// fall outside the buffer range, read zeros without memory traffic and write
+// them into the slot's padding. With no lane-masked load, the compiler's
+// load-counter waits for the staged activations no longer cover chunk loads
+// (Q4_K 28672 x 8192 batch 1: 26.5 -> 25.7 us, shuffled A/B).
+constexpr int kStreamSlot = kStreamLoads * kWave * 16;
 constexpr int kStreamMaxUPL = 2;                   // chunks (units per lane) per row: K <= 8192
 constexpr int kStreamDepth = 2;  // ring slots per wave (measured: faster than 3 at every shape tried)
 // Activation rows per launch. Measured on Q4_K 28672 x 8192: 2 rows 33.1 ->
@@ -1428,16 +1434,13 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   auto issue = [&](int slot) {
     const bool live = issued < n_rows * cpr;
     const int64_t r = irow < N ? irow : N - 1;
-    const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * kStreamSlot,
+    const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * kStreamChunk,
                                 live ? (uint32_t)(chunk_units(ic) * kStreamUnitBytes) : 0u);
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-      // the last load covers the slot's tail only: its other lanes are
-      // switched off, so that nothing is written past the slot
-      if ((k + 1) * kWave * 16 <= kStreamSlot || lane * 16 < kStreamSlot - k * kWave * 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring + slot * kStreamSlot + k * (kWave * 16),
-                                                 16, k * (kWave * 16) + lane * 16, 0, 0,
-                                                 2 /* non-temporal */);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring + slot * kStreamSlot + k * (kWave * 16), 16,
+                                               k * (kWave * 16) + lane * 16, 0, 0,
+                                               2 /* non-temporal */);
     }
     ++issued;
     if (++ic == cpr) {
@@ -1445,28 +1448,79 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
       irow += nwaves;
     }
   };
+  // Stage the activation words and the per-(b, u) sums of gemv_kernel; at
+  // batch 1 each lane then copies those of its first unit into registers.
+  // The barriers wait for LDS operations only, not for chunk requests.
+  // Two orders (shuffled A/B on MI355X, cold HBM):
+  // - Q4_K, and Q4_0 pairs at batch 2: each thread loads its (at most two)
+  //   words before the first chunks are requested, since loads return in
+  //   order and words loaded behind the chunks would wait for them. The
+  //   thread holding the first word of a group of kSumWords words adds the
+  //   group's sums from its neighbours' partial sums (lanes hold a group's
+  //   words in order, and the additions follow word_sums' order), so one
+  //   barrier covers words and sums. Q4_K 28672 x 8192: 25.85 -> 25.5 us
+  //   at batch 1, 32.0 -> 31.2 us at batch 2; Q4_0 12288 x 4096 batch 2:
+  //   10.1 -> 9.65 us.
+  // - Q4_0 pairs at batch 1: chunks first, then gemv_kernel's staging and a
+  //   second pass for the sums. The first order measured 0.3-0.5 us slower
+  //   there (8.0 -> 8.3 us at 11008 and 12288 x 4096).
+  constexpr bool kWordsFirst = !kOneChunk || B == 2;
+  static_assert(kStreamMaxBatch * kStreamMaxUPL * kWave * T <= 2 * kStreamThreads,
+                "two staged words per thread cover every streamed input");
+  if (kWordsFirst) {
+    const int xtotal = B * nu * T;  // at most 2 * kStreamThreads (see the assertion above)
+    XWord xw[2];
+    int xdst[2];
 #pragma unroll
-  for (int k = 0; k < DR; ++k) issue(k);
-
-  // Stage the activation words, then the per-(b, u) sums, as gemv_kernel
-  // does; at batch 1 each lane then copies those of its first unit into
-  // registers. The barriers wait for LDS operations only, not for the chunk
-  // requests above.
-  stage_words<F, kStreamThreads, 1>(xs, B, nu, x, ldx, 0.0625f,
-                                    [&](int b, int u, int t) { return (b * T + t) * NS + u; });
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int i = tid; i < B * nu; i += kStreamThreads) {
-    const int u = i % nu, b = i / nu;
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kStreamThreads;
+      const int ic = i < xtotal ? i : xtotal - 1;
+      const int t = ic % T, r = ic / T;
+      const int b = r % B, u = r / B;
+      xw[k] = load_xword<F>(x, ldx, b, u, t);
+      xdst[k] = i < xtotal ? (b * T + t) * NS + u : -1;
+    }
 #pragma unroll
-    for (int g = 0; g < T / F::kSumWords; ++g) {
+    for (int k = 0; k < DR; ++k) issue(k);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x4 wd = pack_xword(xw[k], 0.0625f);
+      if (xdst[k] >= 0) xs[xdst[k]] = wd;
+      const half2_t ha = as_half2(wd.x), hb = as_half2(wd.y), hc = as_half2(wd.z),
+                    hd = as_half2(wd.w);
+      const float plo = ((float)ha.x + (float)ha.y) + ((float)hc.x + (float)hc.y);
+      const float phi = ((float)hb.x + (float)hb.y) + ((float)hd.x + (float)hd.y);
       float slo = 0.0f, shi = 0.0f;
 #pragma unroll
-      for (int t = g * F::kSumWords; t < (g + 1) * F::kSumWords; ++t)
-        word_sums(xs[(b * T + t) * NS + u], slo, shi);
-      F::stage_sums(sums, i, g, slo, shi);
+      for (int j = 0; j < F::kSumWords; ++j) {
+        slo += __shfl(plo, lane + j < kWave ? lane + j : lane);
+        shi += __shfl(phi, lane + j < kWave ? lane + j : lane);
+      }
+      const int i = tid + k * kStreamThreads;
+      const int t = i % T, r = i / T;
+      if (i < xtotal && t % F::kSumWords == 0)
+        F::stage_sums(sums, (r % B) * nu + r / B, t / F::kSumWords, slo, shi);
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+#pragma unroll
+    for (int k = 0; k < DR; ++k) issue(k);
+    stage_words<F, kStreamThreads, 1>(xs, B, nu, x, ldx, 0.0625f,
+                                      [&](int b, int u, int t) { return (b * T + t) * NS + u; });
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int i = tid; i < B * nu; i += kStreamThreads) {
+      const int u = i % nu, b = i / nu;
+#pragma unroll
+      for (int g = 0; g < T / F::kSumWords; ++g) {
+        float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+        for (int t = g * F::kSumWords; t < (g + 1) * F::kSumWords; ++t)
+          word_sums(xs[(b * T + t) * NS + u], slo, shi);
+        F::stage_sums(sums, i, g, slo, shi);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // At batch 1, registers hold the first chunk's activations; those of a
   // second chunk, and all of them at larger batches, stay in LDS (there are
   // no registers left for them).
