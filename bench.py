@@ -3,6 +3,7 @@
 
 One step runs every hot-path call once, each on synthetic Llama-shaped layer
 inputs already resident in HBM:
+  * Q4_0 decode GEMV, 1024 x 1024, batch 1 (the small configuration);
   * Q4_0 decode GEMV, K = 4096, N = 4096 / 11008 / 12288 (7B layer shapes,
     12288 = fused QKV), batch 1 and 4;
   * Q4_K decode GEMV, K = 8192, N = 28672 (70B FFN), batch 1 and 8;
@@ -16,9 +17,12 @@ Reported (one JSON line on stdout):
                  the step's GEMV launches / the GEMV share of the timed steps
                  (GB/s); every share is timed with HIP events on the launch
                  stream around HIP-graph segments of the step;
-  roofline       the largest decode GEMV (Q4_K 28672 x 8192, batch 1) against
-                 the 8 TB/s HBM peak, timed the same way inside the steps;
-                 traffic from the committed rocprofv3 counter summary;
+  roofline       the dominant GEMV kernel (the GEMV case with the longest
+                 launch) against the 8 TB/s HBM peak, timed the same way
+                 inside the steps; traffic from the committed rocprofv3
+                 counter summary;
+  rooflines      the same figures for every case (GEMVs against HBM, GEMMs
+                 against their matrix-core peaks);
   prefill_gemm   Q8_0 x fp16 GEMM TFLOP/s against the 2.5 PFLOP/s f16 peak;
   fp32_gemm      fp32 GEMM TFLOP/s against the 157.3 TFLOP/s fp32 peak;
   cases          every call timed alone: kernel time, GB/s or TFLOP/s;
@@ -54,8 +58,20 @@ F16_PEAK_TFLOPS = 2500.0       # dense fp16 MFMA
 F32_PEAK_TFLOPS = 157.3        # fp32 matrix
 ROTATE_BYTES = 512 * 2**20     # per weight set: 2x the MALL
 METRIC = "quantized GEMV effective HBM GB/s (% of peak); prefill GEMM TFLOP/s (% MFMA)"
-ROOFLINE_CASE = "q4_k_gemv_28672x8192_b1"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q4_k_gemv_28672x8192_b1.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_cases.json")
+CSRC = os.path.join(ROOT, "block_quantized_matmul_amd", "csrc")
+PROBE_LIB = os.path.join(ROOT, "block_quantized_matmul_amd", "liblqmm_probe.so")
+
+
+def kernel_source_sha256():
+    """Hash over every library source file: a counter summary taken on other
+    sources no longer describes the kernels."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")) and name != "probe.hip":
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
 
 
 def parse():
@@ -66,18 +82,24 @@ def parse():
     # sustained work; 100 untimed steps (about 40 ms) reach the steady state
     # that a serving loop runs in.
     p.add_argument("--warmup", type=int, default=100)
+    # Before the warmup steps, the steps are replayed untimed for at least
+    # this long, so that short warmups (a few steps, well under a
+    # millisecond) also start the timed steps at steady clocks.
+    p.add_argument("--settle-ms", type=float, default=300.0)
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the context figures (counter runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--cases", default="", help="comma-separated subset of case names")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall time of the CPU-oracle baseline sample (whole passes)")
-    p.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "OUT_MD", "COMMAND", "TITLE"),
-                   help="host only: write a markdown summary of a rocprofv3 kernel_stats.csv")
-    p.add_argument("--summarize-traffic", nargs=5,
-                   metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_MIB", "CMD_FETCH", "CMD_WRITE"),
-                   help="host only: write the roofline kernel's HBM traffic summary from two "
-                        "rocprofv3 --pmc counter_collection.csv files")
+    p.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "BENCH_LOG", "OUT_MD", "COMMAND"),
+                   help="host only: write a markdown summary of a rocprofv3 kernel trace of "
+                        "this benchmark (timed launches per case apart from the others)")
+    p.add_argument("--summarize-traffic", nargs=3, metavar=("PMC_DIR", "CALIB_MIB", "COMMAND"),
+                   help="host only: write the GEMV cases' HBM traffic summary from rocprofv3 "
+                        "--pmc runs under PMC_DIR/<case>.fetch and PMC_DIR/<case>.write")
     p.add_argument("--eager", action="store_true",
                    help="launch from Python one call at a time instead of replaying HIP graphs")
     return p.parse_args()
@@ -130,6 +152,27 @@ def build_cases(torch, only):
         return Rot(copies(arr, n))
 
     want = lambda n: not only or n in only
+
+    # Q4_0 decode GEMV, the small configuration (1024 x 1024, batch 1)
+    name = "q4_0_gemv_1024x1024_b1"
+    if want(name):
+        c0 = synth.make("q4_0_gemv_1024")
+        wbytes = c0.W.nbytes
+        R = rot(wbytes)
+        Ws = rotset(c0.W, R)
+        x = torch.from_numpy(c0.x.copy()).to(dev)
+        y = torch.empty((1, c0.N), dtype=torch.float32, device=dev)
+        alg = wbytes + c0.K * 4 + c0.N * 4
+
+        def launch(Ws=Ws, x=x, y=y, N=c0.N):
+            bq.lqmm_gemv_q4_0(Ws.next(), x, N, out=y)
+
+        def launch_warm(W0=Ws.copies[0], x=x, y=y, N=c0.N):
+            bq.lqmm_gemv_q4_0(W0, x, N, out=y)
+
+        cases.append(Case(name, "gemv", alg, 2 * c0.N * c0.K, launch, R,
+                          lambda y=y: y.cpu().numpy(), launch_warm))
+        inputs[name] = ("q4_0", c0.W, c0.x.copy(), c0.N, c0.K)
 
     # Q4_0 decode GEMVs: one weight set per N, shared by batch 1 and 4
     for N in (4096, 11008, 12288):
@@ -245,18 +288,33 @@ def case_summary(c):
 
 
 def traffic_for(case_name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when it is missing or the kernel source changed since it was taken."""
+    """HBM bytes per launch of a case from the committed rocprofv3 counter
+    summary, or None when it is missing or any library source changed since
+    the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    src = os.path.join(ROOT, "block_quantized_matmul_amd", "csrc", "gemv.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if t.get("case") != case_name or t.get("kernel_source_sha256") != h:
+    if t.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("cases", {}).get(case_name, {}).get("hbm_bytes_per_launch")
+
+
+def roofline_entry(c):
+    """Roofline figures of one case: GEMVs against HBM, GEMMs against their
+    matrix-core peak."""
+    ms = c.avg_ms
+    if c.kind == "gemv":
+        ach = c.bytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for(c.name),
+                "algorithmic_bytes_per_launch": c.bytes, "avg_launch_ms": round(ms, 6)}
+    peak = F16_PEAK_TFLOPS if c.kind == "gemm_f16" else F32_PEAK_TFLOPS
+    ach = c.flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "traffic": None, "flops_per_launch": c.flops,
+            "avg_launch_ms": round(ms, 6)}
 
 
 def cpu_model():
@@ -453,64 +511,144 @@ def _short_kernel(name):
     return name
 
 
-def summarize_trace(stats_csv, out_md, command, title):
-    """Markdown table of a `rocprofv3 --kernel-trace --stats` kernel_stats.csv."""
+def _find(dirpath, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(dirpath, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {dirpath}")
+    return hits[-1]
+
+
+def _pct(v, p):
+    """p-th percentile of the sorted list v (linear interpolation)."""
+    if len(v) == 1:
+        return v[0]
+    i = (len(v) - 1) * p / 100.0
+    lo = int(math.floor(i))
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+
+def summarize_trace(trace_dir, bench_log, out_md, command):
+    """Markdown summary of a `rocprofv3 --kernel-trace --stats` run of this
+    benchmark. The timed launches lie between the two marker kernels; they
+    run case-major in the order of the JSON line's "cases", the same number
+    per case, so each case's launches are identified by position. For each
+    case: launches, kernel, mean / median / p10 / p90 duration, and the
+    throughput of the mean against the peak. All other launches (settle,
+    warmup, context) are listed apart, per kernel."""
     import csv
-    rows = list(csv.DictReader(open(stats_csv)))
+    line = None
+    for l in open(bench_log):
+        l = l.strip()
+        if l.startswith("{") and '"metric"' in l:
+            line = json.loads(l)
+    if line is None:
+        raise SystemExit(f"no JSON line in {bench_log}")
+    order = list(line["cases"].keys())
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    b = max(i for i, n in enumerate(names) if "timed_region_begin_marker" in n)
+    e = min(i for i, n in enumerate(names) if "timed_region_end_marker" in n and i > b)
+    timed = rows[b + 1:e]
+    per = len(timed) // len(order)
+    if per * len(order) != len(timed) or per == 0:
+        raise SystemExit(f"{len(timed)} timed launches do not split over {len(order)} cases")
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+    out = []
+    out.append(f"# Kernel trace of `bench.py`: {line['config']['workload']}\n\n")
+    out.append("Command, from the repository root on one MI355X after "
+               "`cd /tmp && export TMPDIR=/tmp` (paths relative to the repository):\n\n")
+    out.append(f"```\n{command}\n```\n\n")
+    out.append(f"Timed region: {len(timed)} launches, {per} per case, between the marker "
+               f"kernels (steps {line['steps']}, warmup {line['warmup']}). Durations are kernel "
+               "start to end from the trace; `bench us` is the same case's mean launch time "
+               "from the HIP events of the bench line (graph replay: it includes the gaps "
+               "between launches).\n\n")
+    out.append("| case | kernel | launches | mean us | median us | p10 us | p90 us | bench us "
+               "| mean rate | of peak |\n|---|---|---:|---:|---:|---:|---:|---:|---:|---:|\n")
+    summary = {}
+    for ci, case in enumerate(order):
+        rs = timed[ci * per:(ci + 1) * per]
+        kn = sorted(set(_short_kernel(r["Kernel_Name"]) for r in rs))
+        d = sorted(dur(r) for r in rs)
+        mean = sum(d) / len(d)
+        cs = line["cases"][case]
+        if "bytes" in cs:
+            rate = cs["bytes"] / (mean * 1e-6) / 1e9
+            rate_s, frac = f"{rate:.0f} GB/s", rate / HBM_PEAK_GBS
+        else:
+            rate = cs["flops"] / (mean * 1e-6) / 1e12
+            peak = F16_PEAK_TFLOPS if case.startswith("q8_0") else F32_PEAK_TFLOPS
+            rate_s, frac = f"{rate:.1f} TFLOP/s", rate / peak
+        summary[case] = {"mean_us": mean, "frac": frac}
+        out.append(f"| {case} | `{' + '.join(kn)}` | {len(d)} | {mean:.2f} | {_pct(d, 50):.2f} | "
+                   f"{_pct(d, 10):.2f} | {_pct(d, 90):.2f} | {cs['ms'] * 1e3:.2f} | {rate_s} | "
+                   f"{frac:.3f} |\n")
+    rf = line.get("roofline", {})
+    if rf.get("case") in summary:
+        out.append(f"\nThe bench line's `roofline` names {rf['case']}: {rf['frac']:.3f} of peak from "
+                   f"the HIP events, {summary[rf['case']]['frac']:.3f} from the trace mean.\n")
+    other = {}
+    for r in rows[:b] + rows[e + 1:]:
+        other.setdefault(_short_kernel(r["Kernel_Name"]), []).append(dur(r))
+    out.append("\nOther launches (settle and warmup replays before the timed region, context "
+               "figures after it; the GEMVs' `warm_same_copy` launches here are cache-resident):\n\n"
+               "| kernel | launches | mean us | median us |\n|---|---:|---:|---:|\n")
+    for k in sorted(other, key=lambda k: -sum(other[k])):
+        d = sorted(other[k])
+        out.append(f"| `{k}` | {len(d)} | {sum(d) / len(d):.2f} | {_pct(d, 50):.2f} |\n")
     with open(out_md, "w") as f:
-        f.write(f"# {title}\n\n")
-        f.write("Command, run from the repository root on one MI355X after "
-                "`cd /tmp && export TMPDIR=/tmp` (paths relative to the repository):\n\n")
-        f.write(f"```\n{command}\n```\n\n")
-        f.write("| kernel | calls | avg us | min us | max us | share % |\n"
-                "|---|---:|---:|---:|---:|---:|\n")
-        for r in rows:
-            f.write(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | "
-                    f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |\n")
+        f.write("".join(out))
+    print("".join(out))
 
 
-def _counter_means(csv_path, counter, pick):
-    """Mean per-dispatch value of `counter` over the dispatches whose kernel
-    name satisfies pick(name)."""
+def _counter_per_dispatch(csv_path, counter):
+    """{dispatch id: (kernel name, summed value of `counter`)}."""
     import csv
-    import collections
-    per = collections.defaultdict(float)
+    per = {}
     for r in csv.DictReader(open(csv_path)):
-        if r["Counter_Name"] == counter and pick(r["Kernel_Name"]):
-            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
-    if not per:
-        raise SystemExit(f"no {counter} dispatches matched in {csv_path}")
-    return sum(per.values()) / len(per), len(per)
+        if r["Counter_Name"] == counter:
+            k = r["Dispatch_Id"]
+            name, v = per.get(k, (r["Kernel_Name"], 0.0))
+            per[k] = (name, v + float(r["Counter_Value"]))
+    return per
 
 
-def summarize_traffic(fetch_csv, write_csv, calib_mib, commands):
-    """HBM bytes per launch of the roofline kernel from a FETCH_SIZE run and a
-    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
-    reads for the calibration kernel (reads and writes calib_mib MiB)."""
-    kern = lambda n: "gemv_stream_kernel<lqmm::(anonymous namespace)::FmtQ4_K" in n
-    calib = lambda n: "neg_kernel" in n
-    f_k, nf = _counter_means(fetch_csv, "FETCH_SIZE", kern)
-    w_k, nw = _counter_means(write_csv, "WRITE_SIZE", kern)
-    f_c, _ = _counter_means(fetch_csv, "FETCH_SIZE", calib)
-    w_c, _ = _counter_means(write_csv, "WRITE_SIZE", calib)
+def summarize_traffic(pmc_dir, calib_mib, command):
+    """HBM bytes per launch of every GEMV case, from one FETCH_SIZE run and
+    one WRITE_SIZE run per case (PMC_DIR/<case>.fetch, PMC_DIR/<case>.write;
+    KiB per dispatch). Each counter is scaled by what it reads for the
+    calibration kernel in the same run (torch.neg over calib_mib MiB, which
+    reads and writes that many bytes). The library's kernels are every
+    dispatch named lqmm:: (the run holds only that case's launches)."""
+    import glob
     expect_kib = calib_mib * 1024.0
-    fs, ws = expect_kib / f_c, expect_kib / w_c
-    src = os.path.join(ROOT, "block_quantized_matmul_amd", "csrc", "gemv.hip")
-    out = {
-        "case": ROOFLINE_CASE,
-        "kernel": "gemv_stream_kernel<FmtQ4_K, ...> (batch 1, rows streamed through LDS)",
-        "kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
-        "dispatches": {"fetch": nf, "write": nw},
-        "fetch_kib_per_dispatch": round(f_k, 1),
-        "write_kib_per_dispatch": round(w_k, 1),
-        "calibration": {"kernel": "torch.neg, float32, out of place", "mib_read": calib_mib,
-                        "mib_written": calib_mib, "fetch_kib": round(f_c, 1),
-                        "write_kib": round(w_c, 1), "fetch_scale": round(fs, 4),
-                        "write_scale": round(ws, 4)},
-        "hbm_bytes_per_launch": int(round((f_k * fs + w_k * ws) * 1024)),
-        "commands": commands,
-    }
+    out = {"kernel_source_sha256": kernel_source_sha256(),
+           "calibration": {"kernel": "torch.neg, float32, out of place",
+                           "mib_read": calib_mib, "mib_written": calib_mib},
+           "command": command, "cases": {}}
+    for d in sorted(glob.glob(os.path.join(pmc_dir, "*.fetch"))):
+        case = os.path.basename(d)[:-len(".fetch")]
+        res = {}
+        for counter, sub in (("FETCH_SIZE", ".fetch"), ("WRITE_SIZE", ".write")):
+            per = _counter_per_dispatch(_find(os.path.join(pmc_dir, case + sub),
+                                              "counter_collection.csv"), counter)
+            kern = [v for n, v in per.values() if "lqmm::" in n and "probe" not in n]
+            cal = [v for n, v in per.values() if "neg_kernel" in n]
+            kname = sorted(set(_short_kernel(n) for n, v in per.values() if "lqmm::" in n))
+            if not kern or not cal:
+                raise SystemExit(f"{case}: no {counter} dispatches of the kernel or calibration")
+            scale = expect_kib / (sum(cal) / len(cal))
+            res[counter] = (sum(kern) / len(kern), len(kern), scale, kname)
+        fk, nf, fs, kname = res["FETCH_SIZE"]
+        wk, nw, wsc, _ = res["WRITE_SIZE"]
+        out["cases"][case] = {
+            "kernel": " + ".join(kname), "dispatches": {"fetch": nf, "write": nw},
+            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+            "fetch_scale": round(fs, 4), "write_scale": round(wsc, 4),
+            "hbm_bytes_per_launch": int(round((fk * fs + wk * wsc) * 1024))}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -520,12 +658,11 @@ def summarize_traffic(fetch_csv, write_csv, calib_mib, commands):
 def main():
     args = parse()
     if args.summarize_trace:
-        stats, out_md, command, title = args.summarize_trace
-        summarize_trace(stats, out_md, command, title)
+        summarize_trace(*args.summarize_trace)
         return
     if args.summarize_traffic:
-        fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write = args.summarize_traffic
-        summarize_traffic(fetch_csv, write_csv, int(calib_mib), [cmd_fetch, cmd_write])
+        pmc_dir, calib_mib, command = args.summarize_traffic
+        summarize_traffic(pmc_dir, int(calib_mib), command)
         return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
@@ -580,23 +717,48 @@ def main():
             if args.warmup:
                 gw = capture(torch, lambda c=c: [c.launch() for _ in range(args.warmup)])
                 warm[c.name] = gw.replay
+    # Settle: replay the steps untimed until --settle-ms of wall time has
+    # passed, so that the clocks have ramped up whatever --warmup is.
+    settle_passes = 0
+    if args.settle_ms > 0:
+        settle = {c.name: (warm.get(c.name) or run[c.name]) for c in order}
+        t_settle = time.perf_counter()
+        while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+            for c in order:
+                settle[c.name]()
+            torch.cuda.synchronize()
+            settle_passes += 1
     for c in order:
         if c.name in warm:
             warm[c.name]()
     torch.cuda.synchronize()
+    # Marker kernels bracket the timed region in kernel traces (outside the
+    # events, so they are not timed).
+    marker = None
+    if os.path.exists(PROBE_LIB):
+        import ctypes
+        plib = ctypes.CDLL(PROBE_LIB)
+        plib.lqmm_probe_marker.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        plib.lqmm_probe_marker.restype = ctypes.c_int
+        marker = lambda w: plib.lqmm_probe_marker(w, torch.cuda.current_stream().cuda_stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+    if marker:
+        marker(0)
     t0 = time.perf_counter()
     ev[0].record()
     for i, c in enumerate(order):
         run[c.name]()
         ev[i + 1].record()
+    if marker:
+        marker(1)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     for i, c in enumerate(order):
         c.avg_ms = ev[i].elapsed_time(ev[i + 1]) / args.steps
         print(f"[bench] {c.name}: {case_summary(c)}", file=sys.stderr, flush=True)
     ms_per_step = sum(c.avg_ms for c in order)
-    roof = [c for c in gemv if c.name == ROOFLINE_CASE]
+    # the dominant GEMV kernel: the GEMV case with the longest launch
+    roof = sorted(gemv, key=lambda c: -c.avg_ms)[:1]
 
     gpu_out = {c.name: c.make_out() for c in gemv}
 
@@ -618,24 +780,20 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "llama_layer_set: Q4_0 GEMV K=4096 N=4096/11008/12288 b1+b4; "
+            "workload": "llama_layer_set: Q4_0 GEMV 1024x1024 b1; "
+                        "Q4_0 GEMV K=4096 N=4096/11008/12288 b1+b4; "
                         "Q4_K GEMV N=28672 K=8192 b1+b8; Q8_0xf16 GEMM 512x14336x4096; "
                         "fp32 GEMM 2048^3",
             "weights": "cold HBM (rotated copies >= 512 MiB per set)",
             "value_is": "GEMV algorithmic bytes / GEMV share of the timed steps (case-major)",
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4) if value else None,
             "wall_ms_per_step_host": round(wall_ms / max(1, args.steps), 4),
+            "settle": {"ms": args.settle_ms, "passes": settle_passes},
         },
     }
     if roof:
-        rc = roof[0]
-        ach = rc.bytes / (rc.avg_ms * 1e-3) / 1e9
-        line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                            "traffic": traffic_for(ROOFLINE_CASE),
-                            "kernel": "gemv_stream_kernel<FmtQ4_K, ...> (" + ROOFLINE_CASE + ")",
-                            "algorithmic_bytes_per_launch": rc.bytes,
-                            "avg_launch_ms": round(rc.avg_ms, 6)}
+        line["roofline"] = dict(roofline_entry(roof[0]), case=roof[0].name)
+    line["rooflines"] = {c.name: roofline_entry(c) for c in order}
     for kind, key, peak in (("gemm_f16", "prefill_gemm", F16_PEAK_TFLOPS),
                             ("gemm_f32", "fp32_gemm", F32_PEAK_TFLOPS)):
         gc = next((c for c in cases if c.kind == kind), None)
@@ -644,10 +802,11 @@ def main():
             line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
                          "ms": round(gc.avg_ms, 6)}
     line["cases"] = {c.name: case_summary(c) for c in order}
-    try:
-        line["context"] = measure_context(torch, cases, stream_sets, args.steps)
-    except Exception as e:  # context only: never costs the measurement above
-        line["context"] = {"error": f"{type(e).__name__}: {e}"}
+    if not args.no_context:
+        try:
+            line["context"] = measure_context(torch, cases, stream_sets, args.steps)
+        except Exception as e:  # context only: never costs the measurement above
+            line["context"] = {"error": f"{type(e).__name__}: {e}"}
 
     if not args.no_cpu_baseline:
         base, worst = cpu_baseline(inputs, gpu_out, args.cpu_seconds)

@@ -12,19 +12,17 @@
 
 namespace {
 
-constexpr int kMaxDevices = 64;
-
 struct DeviceInfo {
   std::once_flag once;
   bool ok = false;
   int num_cus = 0;
 };
-DeviceInfo g_dev[kMaxDevices];
+DeviceInfo g_dev[lqmm::kMaxDevices];
 
 // Current device, checked to be gfx950; CU count cached per device.
 lqmm_status current_device(int *num_cus) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LQMM_ERR_DEVICE;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= lqmm::kMaxDevices) return LQMM_ERR_DEVICE;
   DeviceInfo &di = g_dev[dev];
   std::call_once(di.once, [&]() {
     hipDeviceProp_t prop;

@@ -470,14 +470,8 @@ hipError_t launch_fast(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t
   if (tiles > 0x7fffffff || (int64_t)BM * K * 2 >= ((int64_t)1 << 31) ||
       (int64_t)TT::BN * (K / 32 * 34) >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
-  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_q8_0_kernel<NWAVES>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       TT::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = ensure_max_lds<gemm_q8_0_kernel<NWAVES>>(TT::kLdsBytes);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemm_q8_0_kernel<NWAVES>, dim3((unsigned)tiles), dim3(TT::kThreads),
                      TT::kLdsBytes, stream, W, X, Y, M, N, K, (int)tiles_n);
   return hipGetLastError();

@@ -16,9 +16,12 @@
 //   rows in "chunks" of U units per lane through two register buffers: the
 //   next chunk loads while the current one is computed. The first chunk is
 //   requested before the activations are staged.
-// * Nibbles become fp16 with the exponent trick: OR-ing a nibble into the
-//   mantissa of 1024.0 (0x6400) gives the exact value 1024 + q (low nibble)
-//   or 1024 + 16q (high nibble), one v_and_or_b32 per pair of weights.
+// * Nibbles become fp16 with the exponent trick, one v_and_or_b32 per pair of
+//   weights: a low nibble (bits 0-3 of a 16-bit half) OR-ed into the mantissa
+//   of 1024.0 (0x6400, mantissa step 1) gives exactly 1024 + q; a high nibble
+//   (bits 4-7, mantissa value 16q) OR-ed into the mantissa of 64.0 (0x5400,
+//   mantissa step 1/16) gives exactly 64 + q. The activations therefore stay
+//   unscaled on both halves.
 //
 // VALU mode (batch 1..8, used for 1..2): consecutive lanes take consecutive
 // units of the same row(s) (LPR lanes per row), the activation pairs are
@@ -44,13 +47,14 @@ namespace {
 
 constexpr int kGemvThreads = 512;
 constexpr int kWavesPerWg = kGemvThreads / kWave;
-constexpr uint32_t kMagic = 0x64006400u;  // fp16 pair (1024.0, 1024.0)
+constexpr uint32_t kMagic = 0x64006400u;    // fp16 pair (1024.0, 1024.0): low nibbles
+constexpr uint32_t kMagicHi = 0x54005400u;  // fp16 pair (64.0, 64.0): high nibbles
 constexpr int kCoalrRing = 6;  // chunk slots per wave of gemv_coalr_kernel
 
 // Unpack one 32-bit word of nibbles (bytes e = 0..3, each holding a "lo"
-// nibble and a "hi" nibble) into four fp16 pairs:
-//   p0 = (1024+lo0, 1024+lo2)      p1 = (1024+16hi0, 1024+16hi2)
-//   p2 = (1024+lo1, 1024+lo3)      p3 = (1024+16hi1, 1024+16hi3)
+// nibble and a "hi" nibble) into four fp16 pairs, all exact:
+//   p0 = (1024+lo0, 1024+lo2)      p1 = (64+hi0, 64+hi2)
+//   p2 = (1024+lo1, 1024+lo3)      p3 = (64+hi1, 64+hi3)
 // The staged activation word uses the same order: (x_lo0, x_lo2),
 // (x_hi0, x_hi2), (x_lo1, x_lo3), (x_hi1, x_hi3).
 struct Nibbles {
@@ -69,9 +73,10 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 
 // The unpack constants, materialized once per kernel in VGPRs.
 struct UnpackMasks {
-  uint32_t lo, hi, magic;
-  __device__ __forceinline__ UnpackMasks() : lo(0x000F000Fu), hi(0x00F000F0u), magic(kMagic) {
-    asm volatile("" : "+v"(lo), "+v"(hi), "+v"(magic));
+  uint32_t lo, hi, magic, magic_hi;
+  __device__ __forceinline__ UnpackMasks()
+      : lo(0x000F000Fu), hi(0x00F000F0u), magic(kMagic), magic_hi(kMagicHi) {
+    asm volatile("" : "+v"(lo), "+v"(hi), "+v"(magic), "+v"(magic_hi));
   }
 };
 
@@ -79,9 +84,9 @@ __device__ __forceinline__ Nibbles unpack_word(uint32_t v, const UnpackMasks &k)
   uint32_t v8 = v >> 8;
   Nibbles n;
   n.p0 = as_half2(and_or(v, k.lo, k.magic));
-  n.p1 = as_half2(and_or(v, k.hi, k.magic));
+  n.p1 = as_half2(and_or(v, k.hi, k.magic_hi));
   n.p2 = as_half2(and_or(v8, k.lo, k.magic));
-  n.p3 = as_half2(and_or(v8, k.hi, k.magic));
+  n.p3 = as_half2(and_or(v8, k.hi, k.magic_hi));
   return n;
 }
 
@@ -125,12 +130,13 @@ struct FmtQ4_0 {
   }
   static __device__ __forceinline__ uint32_t word(const Raw &r, int t) { return r.q[t]; }
 
-  // VALU mode. Staged sum per (unit, batch row): -(1032*S_lo + 1152*S_hi) with
-  // S_lo the sum of the staged lo values and S_hi of the staged x/16 hi
-  // values, so that sum_j (q_j - 8) x_j = staged + the dot products.
+  // VALU mode. Staged sum per (unit, batch row): -(1032*S_lo + 72*S_hi) with
+  // S_lo the sum of the staged lo activations and S_hi of the hi ones, so
+  // that sum_j (q_j - 8) x_j = staged + the dot products (which multiply
+  // 1024 + q and 64 + q).
   static __device__ __forceinline__ void stage_sums(float *sums, int idx, int /*g*/, float slo,
                                                     float shi) {
-    sums[idx] = -(1032.0f * slo + 1152.0f * shi);
+    sums[idx] = -(1032.0f * slo + 72.0f * shi);
   }
   // u must index a staged unit; `valid` = 0 makes the unit contribute 0.
   template <int B, int R>
@@ -181,12 +187,12 @@ struct FmtQ4_0 {
   static __device__ __forceinline__ u32x4 dequant(const Raw &r, const Prep &p, int t,
                                                  const UnpackMasks &k) {
     Nibbles n = unpack_word(r.q[t], k);
-    const half2_t lo_bias = h2(-1032.0f), sixteenth = h2(0.0625f), hi_bias = h2(-72.0f);
+    const half2_t lo_bias = h2(-1032.0f), hi_bias = h2(-72.0f);
     u32x4 w;
     w.x = as_u32((n.p0 + lo_bias) * p.d2);
-    w.y = as_u32(pk_fma(n.p1, sixteenth, hi_bias) * p.d2);
+    w.y = as_u32((n.p1 + hi_bias) * p.d2);
     w.z = as_u32((n.p2 + lo_bias) * p.d2);
-    w.w = as_u32(pk_fma(n.p3, sixteenth, hi_bias) * p.d2);
+    w.w = as_u32((n.p3 + hi_bias) * p.d2);
     return w;
   }
   // U consecutive units starting at `unit`, each clamped to `last`.
@@ -264,13 +270,13 @@ struct FmtQ4_K {
     r.q1 = sbp[2 + 2 * (uc & 3)];
     return r;
   }
-  // VALU mode. Staged sums per (unit, batch row): (-1024*S_lo, -1024*S_hi),
-  // which remove the 1024 bias of each dot product and give the activation
-  // sums the dmin * m term needs.
+  // VALU mode. Staged sums per (unit, batch row): (-1024*S_lo, -64*S_hi),
+  // which remove the 1024 and 64 biases of the dot products and give the
+  // activation sums the dmin * m term needs.
   static __device__ __forceinline__ void stage_sums(float *sums, int idx, int /*g*/, float slo,
                                                     float shi) {
     sums[2 * idx] = -1024.0f * slo;
-    sums[2 * idx + 1] = -1024.0f * shi;
+    sums[2 * idx + 1] = -64.0f * shi;
   }
   template <int B, int R>
   static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
@@ -326,7 +332,7 @@ struct FmtQ4_K {
       scale_min(raw[r].h, 2 * pair, sc0, m0);
       scale_min(raw[r].h, 2 * pair + 1, sc1, m1);
       float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1;
-      // -dmin*m*S = dmin*m*(-1024*S)/1024; the hi sum is of x/16 values.
+      // -dmin*m*S = dmin*m*(-1024*S)/1024 (lo) = dmin*m*(-64*S)/64 (hi).
       float dm0 = dmin * (float)m0 * (1.0f / 1024.0f);
       float dm1 = dmin * (float)m1 * (1.0f / 64.0f);
 #pragma unroll
@@ -377,12 +383,12 @@ struct FmtQ4_K {
   static __device__ __forceinline__ u32x4 dequant(const Raw &r, const Prep &p, int t,
                                                  const UnpackMasks &k) {
     Nibbles n = unpack_word(word(r, t), k);
-    const half2_t lo_bias = h2(-1024.0f), sixteenth = h2(0.0625f), hi_bias = h2(-64.0f);
+    const half2_t lo_bias = h2(-1024.0f), hi_bias = h2(-64.0f);
     u32x4 w;
     w.x = as_u32(pk_fma(n.p0 + lo_bias, p.dsc_lo, p.dmm_lo));
-    w.y = as_u32(pk_fma(pk_fma(n.p1, sixteenth, hi_bias), p.dsc_hi, p.dmm_hi));
+    w.y = as_u32(pk_fma(n.p1 + hi_bias, p.dsc_hi, p.dmm_hi));
     w.z = as_u32(pk_fma(n.p2 + lo_bias, p.dsc_lo, p.dmm_lo));
-    w.w = as_u32(pk_fma(pk_fma(n.p3, sixteenth, hi_bias), p.dsc_hi, p.dmm_hi));
+    w.w = as_u32(pk_fma(n.p3 + hi_bias, p.dsc_hi, p.dmm_hi));
     return w;
   }
   // U consecutive units starting at `unit`; four units starting at a
@@ -463,7 +469,7 @@ struct FmtQ4_0x2 {
   // Staged sum per (unit, batch row, block g): as for one Q4_0 block.
   static __device__ __forceinline__ void stage_sums(float *sums, int idx, int g, float slo,
                                                     float shi) {
-    sums[2 * idx + g] = -(1032.0f * slo + 1152.0f * shi);
+    sums[2 * idx + g] = -(1032.0f * slo + 72.0f * shi);
   }
   template <int B, int R>
   static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
@@ -521,8 +527,8 @@ struct FmtQ4_0x2 {
 
 // ---- activation staging ------------------------------------------------------
 // Word (b, u, t) holds the 8 activations of word t of unit u for batch row b,
-// in unpack order; `hi_scale` multiplies the hi values (1/16 in VALU mode so
-// that (1024 + 16q) * x/16 = 64x + qx, 1 in MFMA mode).
+// in unpack order, each rounded to fp16 (no scaling: both nibble halves
+// unpack to exact small integers plus a bias).
 struct XWord {
   float4_t lo, hi;
 };
@@ -533,8 +539,8 @@ __device__ __forceinline__ XWord load_xword(const float *__restrict__ x, int64_t
   return XWord{*reinterpret_cast<const float4_t *>(base + F::x_lo(t)),
                *reinterpret_cast<const float4_t *>(base + F::x_hi(t))};
 }
-__device__ __forceinline__ u32x4 pack_xword(const XWord &w, float hi_scale) {
-  const float4_t hi = w.hi * hi_scale;
+__device__ __forceinline__ u32x4 pack_xword(const XWord &w) {
+  const float4_t hi = w.hi;
   u32x4 word;
   word.x = pack_half2(w.lo.x, w.lo.z);
   word.y = pack_half2(hi.x, hi.z);
@@ -561,7 +567,7 @@ __host__ __device__ __forceinline__ int staged_stride(int n) {
 // unconditional and the compiler waits once per batch, not once per word).
 template <class F, int kThreads, int kBatch, class Slot>
 __device__ __forceinline__ void stage_words(u32x4 *xs, int nb, int nu, const float *__restrict__ x,
-                                            int64_t ldx, float hi_scale, Slot slot) {
+                                            int64_t ldx, Slot slot) {
   constexpr int T = F::kWords;
   const int total = nb * nu * T;
   for (int base = threadIdx.x; base < total; base += kBatch * kThreads) {
@@ -578,7 +584,7 @@ __device__ __forceinline__ void stage_words(u32x4 *xs, int nb, int nu, const flo
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (dst[k] >= 0) xs[dst[k]] = pack_xword(w[k], hi_scale);
+      if (dst[k] >= 0) xs[dst[k]] = pack_xword(w[k]);
   }
 }
 
@@ -646,7 +652,7 @@ gemv_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int
 
   // Stage the words, then the per-(b, u) sums.
   // (one or two words per thread at batch 1 and 2: no batching)
-  stage_words<F, kGemvThreads, 1>(xs, B, nu, x, ldx, 0.0625f,
+  stage_words<F, kGemvThreads, 1>(xs, B, nu, x, ldx,
                                   [&](int b, int u, int t) { return (b * T + t) * NS + u; });
   __syncthreads();
   for (int i = tid; i < B * nu; i += kGemvThreads) {
@@ -797,7 +803,7 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   int c = 0;
   load(buf0, gb + team, 0);
 
-  stage_words<F, kThreads, 4>(xs, nb, nu, x, ldx, 1.0f,
+  stage_words<F, kThreads, 4>(xs, nb, nu, x, ldx,
                               [&](int b, int u, int t) { return t * TS + u * nb + b; });
   __syncthreads();
 
@@ -1028,7 +1034,7 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
     advance(pg, pc);
   }
 
-  stage_words<F, kGemvThreads, 4>(xs, nb, nu, x, ldx, 1.0f,
+  stage_words<F, kGemvThreads, 4>(xs, nb, nu, x, ldx,
                                   [&](int b, int u, int t) { return t * TS + u * nb + b; });
   __syncthreads();
 
@@ -1261,7 +1267,7 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
       }
 #pragma unroll
       for (int k = 0; k < kXB; ++k)
-        if (dst[k] >= 0) xs[dst[k]] = zero[k] ? u32x4{0, 0, 0, 0} : pack_xword(w[k], 1.0f);
+        if (dst[k] >= 0) xs[dst[k]] = zero[k] ? u32x4{0, 0, 0, 0} : pack_xword(w[k]);
     }
     const int xn = n < nb ? n : 0;
 #pragma unroll
@@ -1484,7 +1490,7 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
     for (int k = 0; k < DR; ++k) issue(k);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const u32x4 wd = pack_xword(xw[k], 0.0625f);
+      const u32x4 wd = pack_xword(xw[k]);
       if (xdst[k] >= 0) xs[xdst[k]] = wd;
       const half2_t ha = as_half2(wd.x), hb = as_half2(wd.y), hc = as_half2(wd.z),
                     hd = as_half2(wd.w);
@@ -1505,7 +1511,7 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   } else {
 #pragma unroll
     for (int k = 0; k < DR; ++k) issue(k);
-    stage_words<F, kStreamThreads, 1>(xs, B, nu, x, ldx, 0.0625f,
+    stage_words<F, kStreamThreads, 1>(xs, B, nu, x, ldx,
                                       [&](int b, int u, int t) { return (b * T + t) * NS + u; });
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     for (int i = tid; i < B * nu; i += kStreamThreads) {
@@ -1584,23 +1590,12 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <class K>
-hipError_t set_lds_attr(K kern) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kMaxGemvLds);
-}
-
 template <class F, int B, int DR>
 hipError_t launch_stream(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                          hipStream_t stream) {
   auto kern = gemv_stream_kernel<F, B, DR>;
-  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = ensure_max_lds<gemv_stream_kernel<F, B, DR>>(kMaxLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kStreamThreads), pl.lds_bytes, stream, W,
                      pl.row_bytes, pl.nu, x, pl.ldx, y, pl.ldy, pl.N);
   return hipGetLastError();
@@ -1618,12 +1613,8 @@ template <class F, int B, int R, int U, bool FULL>
 hipError_t launch_valu(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                        hipStream_t stream) {
   auto kern = gemv_kernel<F, B, R, U, FULL>;
-  static bool attr_done = false;  // benign race: setting the attribute twice is harmless
-  if (!attr_done) {
-    hipError_t e = set_lds_attr(kern);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = ensure_max_lds<gemv_kernel<F, B, R, U, FULL>>(kMaxGemvLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, stream, W,
                      pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.lpr_log2,
                      pl.accumulate);
@@ -1634,13 +1625,8 @@ template <class C, int U, int KS, int D>
 hipError_t launch_coal(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                        hipStream_t stream) {
   auto kern = gemv_coal_kernel<C, U, KS, D>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = ensure_max_lds<gemv_coal_kernel<C, U, KS, D>>(kMaxLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, stream, W,
                      pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
                      pl.accumulate);
@@ -1682,13 +1668,8 @@ template <class C, int CPS, int KS>
 hipError_t launch_coalr(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                         hipStream_t stream) {
   auto kern = gemv_coalr_kernel<C, CPS, KS, kCoalrRing>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = ensure_max_lds<gemv_coalr_kernel<C, CPS, KS, kCoalrRing>>(kMaxLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kGemvThreads), pl.lds_bytes, stream, W,
                      pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
                      pl.accumulate);
@@ -1719,12 +1700,8 @@ template <class F, int R, int U, int KS, int NW>
 hipError_t launch_mfma(const GemvPlan &pl, const uint8_t *W, const float *x, float *y,
                        hipStream_t stream) {
   auto kern = gemv_mfma_kernel<F, R, U, KS, NW>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = set_lds_attr(kern);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  const hipError_t e = ensure_max_lds<gemv_mfma_kernel<F, R, U, KS, NW>>(kMaxGemvLds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(NW * kWave), pl.lds_bytes, stream, W,
                      pl.row_bytes, pl.unit0, pl.nu, x, pl.ldx, y, pl.ldy, pl.N, pl.batch,
                      pl.accumulate);

@@ -6,7 +6,34 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace lqmm {
+
+// Devices the per-device state below covers (device ids 0 .. kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+
+// Raise kernel KERN's dynamic-LDS limit to `bytes`, once per device and
+// kernel instance, thread-safe (std::call_once per device); later calls
+// return the first call's result. KERN is a template argument so that every
+// kernel instance has its own flags.
+template <auto KERN>
+hipError_t ensure_max_lds(int bytes) {
+  struct PerDevice {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+  };
+  static PerDevice state[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return hipErrorInvalidDevice;
+  PerDevice &d = state[dev];
+  std::call_once(d.once, [&]() {
+    d.err = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  });
+  return d.err;
+}
 
 // ---- GEMV -------------------------------------------------------------------
 // Q4_0x2: Q4_0 weights taken two blocks (64 weights, 36 bytes) per unit, used

@@ -6,8 +6,9 @@
 //   threads), eight in flight per thread;
 // * wave blocks: each wave reads whole 4 KB blocks (four 1 KB loads of 64
 //   consecutive 16-byte words), the blocks strided over all waves.
-// Built as its own library (liblqmm_probe.so); not part of the lqmm
-// interface.
+// Also two empty marker kernels that bracket the benchmark's timed region in
+// kernel traces. Built as its own library (liblqmm_probe.so); not part of the
+// lqmm interface.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,7 +64,22 @@ block_read_kernel(const u32x4 *__restrict__ p, int64_t n16, uint32_t *out) {
   if (acc == 0x9E3779B9u) out[0] = acc;
 }
 
+// Empty kernels whose names mark the start and the end of the benchmark's
+// timed region in a kernel trace.
+__global__ void timed_region_begin_marker() {}
+__global__ void timed_region_end_marker() {}
+
 }  // namespace
+
+// Launch the begin (which == 0) or end (which != 0) marker kernel on
+// `stream`. Returns 0, or the HIP error code of the launch.
+extern "C" int lqmm_probe_marker(int which, void *stream) {
+  if (which == 0)
+    hipLaunchKernelGGL(timed_region_begin_marker, dim3(1), dim3(64), 0, (hipStream_t)stream);
+  else
+    hipLaunchKernelGGL(timed_region_end_marker, dim3(1), dim3(64), 0, (hipStream_t)stream);
+  return (int)hipGetLastError();
+}
 
 // Read `bytes` (a multiple of 16) from the 16-byte aligned device buffer p on
 // `stream` with `grid` workgroups of 256 threads, in grid-stride order

@@ -11,7 +11,7 @@
 //   accumulators (fp32 products, fp32 accumulation). Measured: 152 -> 144 us
 //   at 2048^3 against eight waves of 64x32; the matrix cores alone (no LDS
 //   reads) take 115 us, so the remaining gap is LDS read latency;
-// * K advances 32 at a time through two LDS buffers: the next tile's global
+// * K advances 64 (BK) at a time through two LDS buffers: the next tile's global
 //   loads are issued before the current tile's MFMAs, and one barrier per step
 //   separates reuse of a buffer;
 // * A is kept k-contiguous in LDS so one ds_read_b128 supplies four MFMA

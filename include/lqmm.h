@@ -26,8 +26,9 @@
  *   arguments are reported without touching the GPU and with nothing
  *   enqueued. Sizes are int64_t; sizes <= 0 are LQMM_ERR_SHAPE (an empty
  *   problem is not a call to make). Outputs must not overlap inputs.
- * - Calls are thread-safe; the only library state is per-device properties
- *   cached on first use.
+ * - Calls are thread-safe and re-entrant: the only library state is set up
+ *   once per device under std::call_once (the device's properties, and each
+ *   kernel's LDS limit on its first launch there).
  * - NaN and Inf inputs propagate; no value is checked.
  *
  * Weight block layouts (llama.cpp / GGUF style). The pages name the formats
@@ -53,14 +54,17 @@
  *
  * Precision
  * ---------
- * Accumulation is fp32 everywhere. The quantized GEMVs round the activations
- * x to fp16 (round to nearest even) before the dot products, so |x| must stay
- * below 65504 and x contributes a relative rounding error of at most 2^-11
- * per element. For one or two activation rows per pass the dequantized
- * weights are exact (the block scales are applied in fp32). From three rows
- * up the GEMVs run on the fp16 matrix cores and round each dequantized
- * weight to fp16: Q4_0 once (d*(q-8)); Q4_K rounds d*sc and dmin*m to fp16
- * once per sub-block and then each weight once (one fused multiply-add).
+ * Accumulation is fp32 everywhere. The quantized GEMVs round each activation
+ * x to fp16 (round to nearest even, no scaling) before the dot products:
+ * |x| must stay below 65504 (larger values become infinite), and in the
+ * fp16 normal range, 2^-14 <= |x| < 65504, x contributes a relative rounding
+ * error of at most 2^-11 per element; smaller |x| are rounded to fp16
+ * subnormals, an absolute error of at most 2^-25 per element. For one or two
+ * activation rows per pass the dequantized weights are exact (the block
+ * scales are applied in fp32). From three rows up the GEMVs run on the fp16
+ * matrix cores and round each dequantized weight to fp16: Q4_0 once
+ * (d*(q-8)); Q4_K rounds d*sc and dmin*m to fp16 once per sub-block and then
+ * each weight once (one fused multiply-add).
  * The Q8_0 GEMM rounds each dequantized weight d*q to fp16 (one rounding)
  * and the output to fp16. The fp32 GEMM uses fp32 matrix-core products with
  * fp32 accumulation.
@@ -119,9 +123,12 @@ lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y,
  * Y = X * W^T. W: N x (K/32) Q8_0 blocks; X: M x K fp16; Y: M x N fp16
  * (fp32 accumulation, rounded to nearest even at the end). K % 32 == 0 and
  * K < LQMM_GEMM_MAX_K.
- * Weight blocks are dequantized to fp16 into LDS and reused by every row
- * of the M tile ("Llamas na Web", "Design de Shader Consciente de
- * Quantizacao", matmul case).
+ * The raw weight blocks of each output tile are loaded into LDS and each
+ * weight is dequantized once per workgroup, in registers, into the fp16
+ * matrix-core operand that every row of the M tile reuses ("Llamas na Web",
+ * "Design de Shader Consciente de Quantizacao", matmul case: blocks loaded
+ * into shared memory, dequantized and reused). When K % 64 == 32 a second
+ * kernel writes dequantized fp16 tiles to LDS instead.
  */
 lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y,
                                int64_t M, int64_t N, int64_t K, void *stream);

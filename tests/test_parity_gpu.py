@@ -317,6 +317,45 @@ def test_q4_k_extreme_codes(orc):
     assert_close(y, orc.gemv_q4_k(W, x, N, K), TOL_QUANT, "q4_k extremes")
 
 
+# Activation scale: the GEMVs round x to fp16 unscaled, so their relative
+# error must not grow when x is small (down to the fp16 subnormal range,
+# 1e-4 * N(0,1)) or large (1e3 * N(0,1), up to ~5e3). Every batch-1/2/4
+# kernel form is forced through the planner's overrides: the streamed and
+# register-loading dot2 kernels (Q4_0 in one- and two-block units), and the
+# matrix-core kernel with activations in LDS and in registers.
+SCALED_FORMS = [
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
+    ("q4_0", 2, {"LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
+    ("q4_0", 2, {"LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_XREGS": "0"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_k", 1, {"LQMM_TUNE_GEMV_STREAM": "1"}),
+    ("q4_k", 1, {"LQMM_TUNE_GEMV_STREAM": "0"}),
+    ("q4_k", 2, {"LQMM_TUNE_GEMV_STREAM": "1"}),
+    ("q4_k", 2, {"LQMM_TUNE_GEMV_STREAM": "0"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_XREGS": "0"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_XREGS": "1"}),
+]
+
+
+@pytest.mark.parametrize("scale", [1e-4, 1e-2, 1e3])
+@pytest.mark.parametrize("fmt,B,env", SCALED_FORMS)
+def test_activation_scale(orc, monkeypatch, scale, fmt, B, env):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    N, K = (300, 4096) if fmt == "q4_0" else (300, 8192)
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(N, K, B, seed=int(N + K + B + 1e4 * scale) % 100003)
+    x = (c.x.astype(np.float64) * scale).astype(np.float32)
+    announce(f"{fmt} gemv N={N} K={K} batch={B} x*{scale:g} {env}")
+    call = bq.lqmm_gemv_q4_k if fmt == "q4_k" else bq.lqmm_gemv_q4_0
+    y = host(call(dev(c.W.reshape(-1)), dev(x), N))
+    ref = (orc.gemv_q4_k if fmt == "q4_k" else orc.gemv_q4_0)(c.W, x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"{fmt} {N}x{K} b{B} x*{scale:g} {env}")
+
+
 # ------------------------------------------------------------- Q8_0 GEMM
 Q8_0_SMALL = [(1, 1, 32), (3, 5, 64), (17, 130, 96), (128, 128, 64), (130, 257, 320),
               (64, 200, 4096), (256, 512, 1024), (1, 300, 32),
@@ -349,16 +388,15 @@ def test_q8_0_tile_widths(orc, monkeypatch, waves, M, N, K):
     assert_close(Y, ref, TOL_QUANT, f"q8_0 {M}x{N}x{K} waves={waves}")
 
 
-def test_q8_0_config_sampled(orc):
+def test_q8_0_config_full(orc):
+    """The prefill configuration at full size, every output element against
+    the oracle (about 3e10 multiply-adds in fp64 on the host cores)."""
     c = synth.make("q8_0_gemm_512x14336x4096")
-    announce("q8_0 gemm 512x14336x4096")
+    announce("q8_0 gemm 512x14336x4096 (all elements)")
     Y = host(bq.lqmm_gemm_q8_0_f16(dev(c.W.reshape(-1)), dev(c.X), c.N)).astype(np.float64)
-    rng = np.random.default_rng(0)
-    cols = np.unique(np.concatenate([[0, 1, 127, 128, 223, 224, 7167, 7168, c.N - 1],
-                                     rng.choice(c.N, 247, replace=False)]))
-    ref = orc.gemm_q8_0_f16(c.W, c.X, c.N, c.K, cols=cols)
-    assert_close(Y[:, cols], ref, TOL_QUANT, "q8_0 config (sampled columns)")
     assert np.isfinite(Y).all()
+    ref = orc.gemm_q8_0_f16(c.W, c.X, c.N, c.K)
+    assert_close(Y, ref, TOL_QUANT, "q8_0 config (all elements)")
 
 
 def test_q8_0_one_hot_exact(orc):
@@ -388,16 +426,14 @@ def test_sgemm_small(orc, M, N, K):
     assert_close(C, ref, TOL_FP32, f"sgemm {M}x{N}x{K}")
 
 
-def test_sgemm_config_sampled(orc):
+def test_sgemm_config_full(orc):
+    """The fp32 configuration at full size (2048^3), every element."""
     s = synth.make("sgemm_2048")
-    announce("sgemm 2048^3")
+    announce("sgemm 2048^3 (all elements)")
     C = host(bq.lqmm_sgemm(dev(s.A), dev(s.B)))
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 1023, 1024, 2047],
-                                     rng.choice(s.M, 55, replace=False)]))
-    ref = orc.sgemm(s.A, s.B, rows=rows)
-    assert_close(C[rows], ref, TOL_FP32, "sgemm config (sampled rows)")
     assert np.isfinite(C).all()
+    ref = orc.sgemm(s.A, s.B)
+    assert_close(C, ref, TOL_FP32, "sgemm config (all elements)")
 
 
 def test_sgemm_identity_exact():
@@ -425,3 +461,62 @@ def test_errors_raise_on_device():
     xn = torch.zeros((2, 64), dtype=torch.float32, device="cuda:0")[:, ::2]
     with pytest.raises(ValueError):
         bq.lqmm_gemv_q4_0(W, xn, 4)
+
+
+_THREADS_SCRIPT = r"""
+import sys, threading
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import block_quantized_matmul_amd as bq
+import synth
+
+torch.cuda.set_device(0)
+a = synth.q4_0_case(1000, 4096, 1, seed=1)
+k = synth.q4_k_case(700, 8192, 8, seed=2)
+g = synth.q8_0_case(130, 300, 512, seed=3)
+s = synth.sgemm_case(150, 130, 70, seed=4)
+d = lambda v: torch.from_numpy(np.ascontiguousarray(v)).cuda()
+calls = [
+    lambda: bq.lqmm_gemv_q4_0(d(a.W.reshape(-1)), d(a.x), a.N),
+    lambda: bq.lqmm_gemv_q4_k(d(k.W.reshape(-1)), d(k.x), k.N),
+    lambda: bq.lqmm_gemv_q4_k(d(k.W.reshape(-1)), d(k.x[:1]), k.N),
+    lambda: bq.lqmm_gemm_q8_0_f16(d(g.W.reshape(-1)), d(g.X), g.N),
+    lambda: bq.lqmm_sgemm(d(s.A), d(s.B)),
+] * 2
+out = [None] * len(calls)
+start = threading.Barrier(len(calls))
+
+def work(i):
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        start.wait()   # every thread's first call to the library at once
+        out[i] = calls[i]()
+    st.synchronize()
+
+ts = [threading.Thread(target=work, args=(i,)) for i in range(len(calls))]
+for t in ts: t.start()
+for t in ts: t.join()
+torch.cuda.synchronize()
+for i, c in enumerate(calls):
+    ref = c().cpu().numpy()
+    assert np.array_equal(out[i].cpu().numpy(), ref), i
+print("threads ok", len(calls))
+"""
+
+
+def test_concurrent_first_calls(tmp_path):
+    """Ten host threads make their first library calls at the same moment, on
+    their own streams, in a fresh process (so every kernel's once-per-device
+    set-up races): each result equals the same call made again serially."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "threads.py"
+    script.write_text(_THREADS_SCRIPT)
+    announce("concurrent first calls (subprocess)")
+    r = subprocess.run([sys.executable, str(script), root], capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "threads ok" in r.stdout
