@@ -150,6 +150,28 @@ def lqmm_sgemm(A, B, out=None, stream=None):
     return out
 
 
+# Split-K workspaces the binding provides when the caller passes none: one
+# zero-filled buffer per (device, stream), grown on demand. Every completed
+# library call leaves the bytes it used zero again, so a buffer stays
+# reusable; calls on different streams never share one.
+_workspaces = {}
+
+
+def _default_workspace(device, stream_handle, nbytes):
+    torch = _torch()
+    key = (device.index, int(stream_handle or 0))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        # The fill runs on the current stream; make it complete before any
+        # other stream uses the buffer (under graph capture the fill is part
+        # of the graph, on the capturing stream, and nothing may synchronize).
+        if not torch.cuda.is_current_stream_capturing():
+            torch.cuda.synchronize(device)
+        _workspaces[key] = ws
+    return ws
+
+
 def _gemv(fn, blk, blk_bytes, W, x, N, out, workspace, stream):
     torch = _torch()
     _dev_tensor(W, torch.uint8, "W")
@@ -170,18 +192,26 @@ def _gemv(fn, blk, blk_bytes, W, x, N, out, workspace, stream):
         raise ValueError("out has the wrong size")
     _same_device(W, x, out)
     ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        _dev_tensor(workspace, torch.uint8, "workspace")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     with torch.cuda.device(x.device):
-        _check(fn(W.data_ptr(), x2.data_ptr(), out.data_ptr(), N, K, batch, ws_ptr, ws_bytes,
-                  _stream(stream)))
+        st = _stream(stream)
+        if workspace is None:
+            need = load().lqmm_gemv_workspace_bytes(N, K, batch)
+            if need:
+                workspace = _default_workspace(x.device, st, need)
+        elif workspace is False:  # explicitly none: plans that need one are not used
+            workspace = None
+        if workspace is not None:
+            _dev_tensor(workspace, torch.uint8, "workspace")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+        _check(fn(W.data_ptr(), x2.data_ptr(), out.data_ptr(), N, K, batch, ws_ptr, ws_bytes, st))
     return out.view(-1) if squeeze and out.dim() == 2 and out.shape[0] == 1 else out
 
 
 def lqmm_gemv_q4_0(W, x, N, out=None, workspace=None, stream=None):
     """y = x @ W^T with W an N x K matrix of Q4_0 blocks; x (batch, K) or (K,)
-    fp32 -> y (batch, N) (or (N,)) fp32."""
+    fp32 -> y (batch, N) (or (N,)) fp32. workspace: a uint8 device tensor
+    (zero-filled before first use) for split-K plans; None lets the binding
+    provide one per device and stream; False passes none."""
     return _gemv(load().lqmm_gemv_q4_0, 32, Q4_0_BLOCK_BYTES, W, x, N, out, workspace, stream)
 
 

@@ -46,18 +46,132 @@ int env_int(const char *name) {
   return atoi(s);
 }
 
+// ---- small problems -----------------------------------------------------------
+// The latency-bound kernel takes problems of at most this many 64-weight
+// units (4096 x 4096 Q4_0: 262,144 units, 9.4 MB) at up to four activation
+// rows: there the whole matrix is a few memory round trips' worth of data.
+constexpr int64_t kSmallMaxUnits = 262144;
+// Activation rows it takes by default; up to kSmallMaxBatch when forced
+// (LQMM_TUNE_GEMV_SMALL=1). Measured at 4096 x 4096 Q4_0: batch 1 5.75 ->
+// 5.54 us against the kernels below, batch 4 6.7 -> 10.3 us (the dot2 work
+// grows with the rows; the matrix cores take it from three rows up).
+constexpr int kSmallBatch = 2;
+constexpr int kSmallMaxBatch = 4;
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Plan the small-problem kernel for one pass of B <= 4 activation rows.
+// Slices: the fewest (a power of two) that let one wave cover a row slice
+// (at most 64 lanes x U units); LQMM_TUNE_GEMV_SPLITK forces more. Waves per
+// workgroup: the most (4, 2, 1) that still give every CU a workgroup.
+// Returns false when the problem is not small (or the override disables the
+// kernel); the workspace the plan needs is *ws_need (0 for one slice).
+bool plan_small(lqmm::GemvFormat fmt, int64_t N, int64_t K, int B, int num_cus,
+                lqmm::SmallGemvPlan *pl, size_t *ws_need) {
+  using lqmm::GemvFormat;
+  const int env_small = env_int("LQMM_TUNE_GEMV_SMALL");
+  const int env_splitk = env_int("LQMM_TUNE_GEMV_SPLITK");
+  const int env_u = env_int("LQMM_TUNE_GEMV_SMALL_U");
+  const int env_nw = env_int("LQMM_TUNE_GEMV_SMALL_WAVES");
+  if (env_small == 0 || B < 1 || B > (env_small == 1 ? kSmallMaxBatch : kSmallBatch)) return false;
+  const GemvFormat f = fmt == GemvFormat::Q4_0 && K % 64 == 0 ? GemvFormat::Q4_0x2 : fmt;
+  const int uw = lqmm::gemv_unit_weights(f);
+  const int64_t nu64 = K / uw;
+  if (env_small != 1 && N * (K / 64) > kSmallMaxUnits) return false;
+  if (nu64 > (1 << 24)) return false;
+  const int nu = (int)nu64;
+  const int U = env_u == 2 ? 2 : 1;
+  const int step = f == GemvFormat::Q4_K ? 4 : 1;  // Q4_K slices start on super-blocks
+  auto slice_units = [&](int S) {
+    int n = (nu + S - 1) / S;
+    return (n + step - 1) / step * step;
+  };
+  int S = 1;
+  while (slice_units(S) > 64 * U) S *= 2;
+  if (env_splitk > S) S = env_splitk;
+  int nus = slice_units(S);
+  S = (nu + nus - 1) / nus;  // slices actually covered
+  int lpr_log2 = 0;
+  while ((1 << lpr_log2) * U < nus) ++lpr_log2;
+  const int rows_per_wave = 64 >> lpr_log2;
+  const size_t lds = lqmm::gemv_small_lds_bytes(f, B, nus);
+  if (lds > lqmm::gemv_small_max_lds()) return false;
+  auto blocks = [&](int nw) { return (N + (int64_t)rows_per_wave * nw - 1) / ((int64_t)rows_per_wave * nw); };
+  // The widest workgroups that still leave a quarter of the CUs one: each
+  // workgroup stages its x slice once, so wider ones move less from L2, and
+  // these problems are bound by latency, not by the CUs' load bandwidth.
+  // Measured at batch 1: 4096 x 4096 with 4096 one-wave workgroups 7.6 us,
+  // 2048 two-wave 6.1, 1024 four-wave 5.5, 512 eight-wave 5.35, 256
+  // sixteen-wave 5.15; 1024 x 1024 with 256 one-wave workgroups 3.9-4.2 us,
+  // 64 four-wave 3.66, 32 eight-wave 3.75. 8 and 16 waves for one unit per
+  // lane at one or two rows.
+  const bool wide = U == 1 && B <= 2;
+  int nw = 1;
+  for (int c : {16, 8, 4, 2}) {
+    if ((c <= 4 || wide) && blocks(c) * S * 4 >= num_cus) {
+      nw = c;
+      break;
+    }
+  }
+  if (env_nw == 1 || env_nw == 2 || env_nw == 4 || (wide && (env_nw == 8 || env_nw == 16)))
+    nw = env_nw;
+  const int64_t rb = blocks(nw);
+  if (rb * S > 0x7fffffff) return false;
+  pl->f = f;
+  pl->batch = B;
+  pl->units_per_lane = U;
+  pl->lpr_log2 = lpr_log2;
+  pl->slices = S;
+  pl->nu = nu;
+  pl->nus = nus;
+  pl->waves = nw;
+  pl->row_blocks = (int)rb;
+  pl->grid = (int)(rb * S);
+  pl->lds_bytes = lds;
+  pl->row_bytes = f == GemvFormat::Q4_K ? K / 256 * 144 : K / 32 * 18;
+  pl->N = N;
+  // counters (one int per row block), then S * B * N partial sums
+  *ws_need = S == 1 ? 0 : align_up((size_t)rb * 4) + (size_t)S * B * (size_t)N * 4;
+  return true;
+}
+
 lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, float *y,
-                        int64_t N, int64_t K, int64_t batch, hipStream_t stream) {
+                        int64_t N, int64_t K, int64_t batch, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
   using lqmm::GemvFormat;
   const int blk = fmt == GemvFormat::Q4_0 ? 32 : 256;
   const int blk_bytes = fmt == GemvFormat::Q4_0 ? 18 : 144;
   if (!W || !x || !y) return LQMM_ERR_NULL;
   if (!dim_ok(N) || !dim_ok(K) || !dim_ok(batch) || K % blk != 0) return LQMM_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(x) || !aligned16(y)) return LQMM_ERR_ALIGN;
+  if (ws && !aligned16(ws)) return LQMM_ERR_ALIGN;
 
   int num_cus = 0;
   lqmm_status st = current_device(&num_cus);
   if (st != LQMM_OK) return st;
+
+  // Small problems (all rows in passes of at most four): the latency-bound
+  // kernel, when its split-K workspace (if it needs one) is there.
+  if (batch <= kSmallMaxBatch) {  // (plan_small applies the default limit)
+    lqmm::SmallGemvPlan sp;
+    size_t need = 0;
+    if (plan_small(fmt, N, K, (int)batch, num_cus, &sp, &need)) {
+      if (need > 0 && (!ws || ws_bytes < need)) {
+        if (env_int("LQMM_TUNE_GEMV_SPLITK") > 1) return LQMM_ERR_WORKSPACE;
+      } else {
+        sp.ldx = K;
+        sp.ldy = N;
+        int *cnt = need ? static_cast<int *>(ws) : nullptr;
+        float *part = need ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                       align_up((size_t)sp.row_blocks * 4))
+                           : nullptr;
+        hipError_t e = lqmm::gemv_small_launch(sp, static_cast<const uint8_t *>(W), x, y, part,
+                                               cnt, stream);
+        return e == hipSuccess ? LQMM_OK : LQMM_ERR_LAUNCH;
+      }
+    }
+  }
 
   const int64_t units_total = K / lqmm::gemv_unit_weights(fmt);
   const int64_t row_bytes = K / blk * blk_bytes;
@@ -316,16 +430,14 @@ lqmm_status lqmm_sgemm(const float *A, const float *B, float *C, int64_t M, int6
 
 lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y, int64_t N, int64_t K,
                            int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return gemv_common(lqmm::GemvFormat::Q4_0, W, x, y, N, K, batch, (hipStream_t)stream);
+  return gemv_common(lqmm::GemvFormat::Q4_0, W, x, y, N, K, batch, workspace, workspace_bytes,
+                     (hipStream_t)stream);
 }
 
 lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y, int64_t N, int64_t K,
                            int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  return gemv_common(lqmm::GemvFormat::Q4_K, W, x, y, N, K, batch, (hipStream_t)stream);
+  return gemv_common(lqmm::GemvFormat::Q4_K, W, x, y, N, K, batch, workspace, workspace_bytes,
+                     (hipStream_t)stream);
 }
 
 lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, int64_t M,
@@ -343,10 +455,17 @@ lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, in
 }
 
 size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
-  (void)N;
-  (void)K;
-  (void)batch;
-  return 0;
+  // The larger of the two formats' needs (a Q4_0 and a Q4_K call of these
+  // sizes), for the most row blocks any device's plan can have.
+  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(batch) || batch > kSmallMaxBatch) return 0;
+  size_t best = 0;
+  for (lqmm::GemvFormat f : {lqmm::GemvFormat::Q4_0, lqmm::GemvFormat::Q4_K}) {
+    if (K % (f == lqmm::GemvFormat::Q4_K ? 256 : 32) != 0) continue;
+    lqmm::SmallGemvPlan sp;
+    size_t need = 0;
+    if (plan_small(f, N, K, (int)batch, 1 << 30, &sp, &need) && need > best) best = need;
+  }
+  return best;
 }
 
 const char *lqmm_status_string(lqmm_status s) {

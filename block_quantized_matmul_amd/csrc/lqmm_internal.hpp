@@ -85,6 +85,29 @@ int gemv_threads();
 hipError_t gemv_launch(GemvFormat f, const GemvPlan &plan, const uint8_t *W, const float *x,
                        float *y, hipStream_t stream);
 
+// Latency-bound kernel for small problems (gemv_small.hip): one workgroup of
+// `waves` waves per (row block, K slice); each lane takes units_per_lane
+// units of its row's slice; slices > 1 splits K across workgroups (partial
+// sums in a workspace, fixed-order reduction by the last arrival).
+struct SmallGemvPlan {
+  GemvFormat f;       // Q4_0, Q4_0x2 or Q4_K
+  int batch;          // activation rows (1..4)
+  int units_per_lane; // 1 or 2
+  int lpr_log2;       // log2(lanes per row)
+  int slices;         // K slices (workgroups per row block)
+  int nu;             // units per row
+  int nus;            // units per slice
+  int waves;          // waves per workgroup: 1, 2 or 4
+  int grid;           // workgroups = row blocks * slices
+  int row_blocks;
+  size_t lds_bytes;
+  int64_t row_bytes, ldx, ldy, N;
+};
+size_t gemv_small_lds_bytes(GemvFormat f, int batch, int nus);
+size_t gemv_small_max_lds();  // the most dynamic LDS a small-kernel plan may use
+hipError_t gemv_small_launch(const SmallGemvPlan &plan, const uint8_t *W, const float *x, float *y,
+                             float *partials, int *counters, hipStream_t stream);
+
 // ---- Q8_0 x fp16 GEMM ---------------------------------------------------------
 hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,
                             int64_t N, int64_t K, int num_cus, hipStream_t stream);

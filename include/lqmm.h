@@ -111,8 +111,15 @@ lqmm_status lqmm_sgemm(const float *A, const float *B, float *C,
  * to 16 per pass on the matrix cores, which take over from 3 rows).
  * Dequantization happens in registers ("Llamas na Web", "Design de Shader
  * Consciente de Quantizacao", mat-vec case).
- * workspace/workspace_bytes: optional device scratch; pass NULL/0. The
- * current kernels need none (lqmm_gemv_workspace_bytes returns 0).
+ * workspace/workspace_bytes: device memory for split-K plans, which split a
+ * row's K range over several workgroups (on different CUs) and add their
+ * partial sums in a fixed order (results do not depend on timing). At least
+ * lqmm_gemv_workspace_bytes(N, K, batch) bytes, 16-byte aligned, owned by
+ * the caller, zero-filled once before its first use: every completed call
+ * leaves the bytes it used (arrival counters and partial sums) zero again. Calls that may run at the same
+ * time (other streams, other threads) must not share a workspace. NULL (or
+ * too few bytes) is valid: the planner then uses no split-K plan, except
+ * when a tuning override forces one (LQMM_ERR_WORKSPACE).
  */
 lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y,
                            int64_t N, int64_t K, int64_t batch,
@@ -143,7 +150,8 @@ lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y,
                            int64_t N, int64_t K, int64_t batch,
                            void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace the GEMV calls can use for these sizes, in bytes (0 = none). */
+/* Workspace the GEMV calls of these sizes can use, in bytes (0 = none):
+ * enough for lqmm_gemv_q4_0 and lqmm_gemv_q4_k on any device. */
 size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch);
 
 /* Static, human-readable name of a status code. */

@@ -69,8 +69,30 @@ def test_status_strings(lib):
     assert bq.lqmm_version() >= 100
 
 
-def test_workspace_query(lib):
+def test_workspace_query(lib, monkeypatch):
+    """The split-K workspace the planner asks for: none when one wave covers
+    a row slice; for longer rows one arrival counter per row block (256-byte
+    aligned) and S * batch * N fp32 partial sums."""
+    monkeypatch.delenv("LQMM_TUNE_GEMV_SPLITK", raising=False)
     assert bq.lqmm_gemv_workspace_bytes(4096, 4096, 1) == 0
+    assert bq.lqmm_gemv_workspace_bytes(1024, 1024, 1) == 0
+    # K = 8192: 128 units of 64 weights, two slices of 64; one row per wave
+    # and one wave per workgroup at most: 100 counters
+    assert bq.lqmm_gemv_workspace_bytes(100, 8192, 2) == 512 + 2 * 2 * 100 * 4
+    # K = 16384 Q4_K: four slices
+    assert bq.lqmm_gemv_workspace_bytes(64, 16384, 1) == 256 + 4 * 1 * 64 * 4
+    # not a small problem, or more than four activation rows: none
+    assert bq.lqmm_gemv_workspace_bytes(28672, 8192, 1) == 0
+    assert bq.lqmm_gemv_workspace_bytes(100, 8192, 5) == 0
+    # a forced split at a configuration shape: 1024 x 1024 in two slices of
+    # 8 units (8 lanes per row, 8 rows per wave: 128 counters)
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SPLITK", "2")
+    assert bq.lqmm_gemv_workspace_bytes(1024, 1024, 1) == 512 + 2 * 1 * 1024 * 4
+
+
+def test_workspace_alignment_checked(lib):
+    f = lib.lqmm_gemv_q4_0
+    assert f(A16, A16, A16, 8, 64, 1, A8, 4096, None) == ERR_ALIGN
 
 
 # Fake but 16-byte aligned addresses: validation rejects the call before any

@@ -48,8 +48,13 @@ Q4_0_SMALL = [(1, 32, 1), (7, 32, 3), (5, 64, 2), (13, 96, 1), (33, 288, 5), (64
               (3, 36864, 4), (4096, 4096, 4)]
 
 
+# Each shape with the planner's choice, and with the small-problem kernel
+# switched off (so that the shapes it takes also reach the other kernels).
+@pytest.mark.parametrize("small", ["default", "0"])
 @pytest.mark.parametrize("N,K,B", Q4_0_SMALL)
-def test_q4_0_small(orc, N, K, B):
+def test_q4_0_small(orc, monkeypatch, small, N, K, B):
+    if small != "default":
+        monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", small)
     c = synth.q4_0_case(N, K, B, seed=N * 7 + K + B)
     announce(f"q4_0 gemv N={N} K={K} batch={B}")
     y = _run_q4_0(c)
@@ -65,6 +70,8 @@ def test_q4_0_small(orc, N, K, B):
 def test_q4_0_dot2_units(orc, monkeypatch, pair, N, K, B):
     # the dot2 path (batch <= 2) with one block per unit and with two (taken
     # only when K % 64 == 0), forced through the planner's tuning override
+    # (the small-problem kernel, which would take most of these, is off)
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
     monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", str(pair))
     c = synth.q4_0_case(N, K, B, seed=N * 5 + K + B + pair)
     announce(f"q4_0 gemv N={N} K={K} batch={B} pair={pair}")
@@ -108,7 +115,7 @@ def test_q4_0_one_hot_exact(orc, monkeypatch, pair):
     assert np.array_equal(y, ref.astype(np.float16).astype(np.float32))
 
 
-def test_q4_0_subnormal_scales(orc):
+def test_q4_0_subnormal_scales(orc, monkeypatch):
     """Subnormal fp16 scales are honoured (not flushed)."""
     N, K = 64, 256
     rng = np.random.default_rng(5)
@@ -118,14 +125,27 @@ def test_q4_0_subnormal_scales(orc):
     x = np.eye(K, dtype=np.float32)[[0, 20, 77, 255]]
     announce("q4_0 subnormal scales")
     ref = orc.gemv_q4_0(W, x, N, K)
-    for i in (0, 2):   # dot2 path: exact
-        y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x[i:i + 2]), N))
-        assert np.array_equal(y, ref[i:i + 2].astype(np.float32))
-    y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x), N))  # matrix cores
+    # dot2 arithmetic (exact): the small-problem kernel at two and (forced)
+    # four rows, and the other batch-1/2 kernels
+    for small in ("", "0"):
+        if small:
+            monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", small)
+        for i in (0, 2):
+            y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x[i:i + 2]), N))
+            assert np.array_equal(y, ref[i:i + 2].astype(np.float32))
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "1")
+    y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x), N))
+    assert np.array_equal(y, ref.astype(np.float32))
+    # the matrix cores (each weight rounded once to fp16)
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
+    y = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(x), N))
     assert np.array_equal(y, ref.astype(np.float16).astype(np.float32))
     xr = rng.standard_normal((2, K)).astype(np.float32)
     y2 = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(xr), N))
     assert_close(y2, orc.gemv_q4_0(W, xr, N, K), TOL_QUANT, "subnormal random x")
+    monkeypatch.delenv("LQMM_TUNE_GEMV_SMALL")
+    y2 = host(bq.lqmm_gemv_q4_0(dev(W.reshape(-1)), dev(xr), N))
+    assert_close(y2, orc.gemv_q4_0(W, xr, N, K), TOL_QUANT, "subnormal random x, small kernel")
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q4_k"])
@@ -169,8 +189,11 @@ Q4_K_SMALL = [(1, 256, 1), (3, 512, 2), (17, 768, 8), (5, 256, 9), (9, 8704, 8),
               (3, 147456, 1)]
 
 
+@pytest.mark.parametrize("small", ["default", "0"])
 @pytest.mark.parametrize("N,K,B", Q4_K_SMALL)
-def test_q4_k_small(orc, N, K, B):
+def test_q4_k_small(orc, monkeypatch, small, N, K, B):
+    if small != "default":
+        monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", small)
     c = synth.q4_k_case(N, K, B, seed=N * 3 + K + B)
     announce(f"q4_k gemv N={N} K={K} batch={B}")
     y = _run_q4_k(c)
@@ -196,6 +219,7 @@ COAL_CASES = [("q4_k", 17, 256, 3, {}), ("q4_k", 33, 768, 8, {}), ("q4_k", 100, 
 @pytest.mark.parametrize("xregs", [0, 1])
 @pytest.mark.parametrize("fmt,N,K,B,env", COAL_CASES)
 def test_coal_forms(orc, monkeypatch, xregs, fmt, N, K, B, env):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
     monkeypatch.setenv("LQMM_TUNE_GEMV_XREGS", str(xregs))  # 1 forces it where it fits
     for k, v in env.items():
         monkeypatch.setenv(k, v)
@@ -220,6 +244,7 @@ STREAM_CASES = [(1, 256, 1), (5, 1280, 2), (2049, 512, 1), (300, 4352, 1), (77, 
 @pytest.mark.parametrize("stream", [0, 1])
 @pytest.mark.parametrize("N,K,B", STREAM_CASES)
 def test_q4_k_dot2_forms(orc, monkeypatch, stream, N, K, B):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
     monkeypatch.setenv("LQMM_TUNE_GEMV_STREAM", str(stream))
     c = synth.q4_k_case(N, K, B, seed=N + 5 * K + B + stream)
     announce(f"q4_k gemv N={N} K={K} batch={B} stream={stream}")
@@ -238,6 +263,7 @@ def test_stream_matches_register_kernel(monkeypatch, fmt, K, B):
     c = make(300, K, B, seed=77 + K + B)
     W, x = dev(c.W.reshape(-1)), dev(c.x)
     call = bq.lqmm_gemv_q4_k if fmt == "q4_k" else bq.lqmm_gemv_q4_0
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
     monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", "1")
     announce(f"{fmt} stream vs register kernel, K={K}")
     ys = []
@@ -257,6 +283,7 @@ Q4_0_STREAM_CASES = [(1, 64, 1), (300, 2048, 1), (8193, 1024, 1), (9000, 4096, 1
 @pytest.mark.parametrize("stream", [0, 1])
 @pytest.mark.parametrize("N,K,B", Q4_0_STREAM_CASES)
 def test_q4_0_dot2_forms(orc, monkeypatch, stream, N, K, B):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
     monkeypatch.setenv("LQMM_TUNE_GEMV_STREAM", str(stream))
     monkeypatch.setenv("LQMM_TUNE_GEMV_Q4_0_PAIR", "1")
     c = synth.q4_0_case(N, K, B, seed=N + 7 * K + stream)
@@ -317,26 +344,118 @@ def test_q4_k_extreme_codes(orc):
     assert_close(y, orc.gemv_q4_k(W, x, N, K), TOL_QUANT, "q4_k extremes")
 
 
+# Small problems: the latency-bound kernel (one round trip to memory), with K
+# split across workgroups where a row slice exceeds one wave (long K) or
+# where the tuning override forces it (LQMM_TUNE_GEMV_SPLITK), including
+# the configuration shapes; ragged N, K % 64 == 32 (single-block Q4_0
+# units), one to four activation rows (three and four forced), one to
+# sixteen waves per workgroup, one and two units per lane.
+SMALL_CASES = [
+    ("q4_0", 1024, 1024, 1, {}),
+    ("q4_0", 1024, 1024, 1, {"LQMM_TUNE_GEMV_SPLITK": "2"}),
+    ("q4_0", 1024, 1024, 1, {"LQMM_TUNE_GEMV_SPLITK": "4"}),
+    ("q4_0", 4096, 4096, 1, {}),
+    ("q4_0", 4096, 4096, 1, {"LQMM_TUNE_GEMV_SPLITK": "2"}),
+    ("q4_0", 4096, 4096, 2, {"LQMM_TUNE_GEMV_SMALL_WAVES": "8"}),
+    ("q4_0", 4096, 4096, 4, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SPLITK": "4"}),
+    ("q4_0", 4096, 4096, 3, {"LQMM_TUNE_GEMV_SMALL": "1"}),
+    ("q4_0", 777, 1056, 2, {"LQMM_TUNE_GEMV_SPLITK": "4"}),
+    ("q4_0", 33, 96, 1, {"LQMM_TUNE_GEMV_SMALL": "1"}),
+    ("q4_0", 100, 8192, 2, {}),
+    ("q4_0", 50, 16384, 3, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SMALL_U": "2"}),
+    ("q4_0", 129, 2048, 4, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SMALL_WAVES": "1"}),
+    ("q4_0", 129, 2048, 2, {"LQMM_TUNE_GEMV_SMALL_WAVES": "2", "LQMM_TUNE_GEMV_SPLITK": "8"}),
+    ("q4_0", 3000, 2048, 1, {"LQMM_TUNE_GEMV_SMALL_WAVES": "16", "LQMM_TUNE_GEMV_SPLITK": "2"}),
+    ("q4_k", 1000, 4096, 1, {}),
+    ("q4_k", 513, 8192, 2, {}),
+    ("q4_k", 513, 8192, 4, {"LQMM_TUNE_GEMV_SMALL": "1"}),
+    ("q4_k", 300, 2048, 2, {"LQMM_TUNE_GEMV_SPLITK": "8"}),
+    ("q4_k", 64, 16384, 1, {}),
+    ("q4_k", 7, 256, 3, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SPLITK": "2"}),
+    ("q4_k", 90, 4352, 4, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SMALL_U": "2",
+                           "LQMM_TUNE_GEMV_SPLITK": "2"}),
+    ("q4_k", 1100, 2048, 2, {"LQMM_TUNE_GEMV_SMALL_WAVES": "16"}),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,B,env", SMALL_CASES)
+def test_small_kernel(orc, monkeypatch, fmt, N, K, B, env):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(N, K, B, seed=3 * N + K + B + len(env))
+    announce(f"{fmt} small gemv N={N} K={K} batch={B} {env}")
+    y = _run_q4_k(c) if fmt == "q4_k" else _run_q4_0(c)
+    ref = (orc.gemv_q4_k if fmt == "q4_k" else orc.gemv_q4_0)(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"{fmt} small {N}x{K} b{B} {env}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_k"])
+def test_small_split_fixed_order(monkeypatch, fmt):
+    """Split-K results are added in slice order, whatever order the
+    workgroups finish in: repeated calls are bitwise equal (the second and
+    later ones also rely on the arrival counters being back at zero), and so
+    are calls with other workgroup widths (each slice's partial sums do not
+    depend on them)."""
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(1000, 4096, 2, seed=12)
+    call = bq.lqmm_gemv_q4_k if fmt == "q4_k" else bq.lqmm_gemv_q4_0
+    W, x = dev(c.W.reshape(-1)), dev(c.x)
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SPLITK", "4")
+    announce(f"{fmt} split-K fixed order")
+    ys = [host(call(W, x, c.N)) for _ in range(4)]
+    for nw in ("1", "2", "4"):
+        monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL_WAVES", nw)
+        ys.append(host(call(W, x, c.N)))
+    for y in ys[1:]:
+        assert np.array_equal(y, ys[0])
+
+
+def test_small_split_needs_workspace(monkeypatch):
+    """A forced split-K plan without a workspace is refused; without the
+    override the planner runs a plan that needs none."""
+    c = synth.q4_0_case(256, 4096, 1, seed=4)
+    W, x = dev(c.W.reshape(-1)), dev(c.x)
+    announce("split-K workspace errors")
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SPLITK", "2")
+    with pytest.raises(bq.LqmmError) as e:
+        bq.lqmm_gemv_q4_0(W, x, c.N, workspace=False)
+    assert e.value.status == 4
+    import torch
+    small_ws = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(bq.LqmmError):
+        bq.lqmm_gemv_q4_0(W, x, c.N, workspace=small_ws)
+    monkeypatch.delenv("LQMM_TUNE_GEMV_SPLITK")
+    y = host(bq.lqmm_gemv_q4_0(W, x, c.N, workspace=False))
+    y2 = host(bq.lqmm_gemv_q4_0(W, x, c.N))
+    assert np.array_equal(y, y2)
+
+
 # Activation scale: the GEMVs round x to fp16 unscaled, so their relative
 # error must not grow when x is small (down to the fp16 subnormal range,
 # 1e-4 * N(0,1)) or large (1e3 * N(0,1), up to ~5e3). Every batch-1/2/4
 # kernel form is forced through the planner's overrides: the streamed and
-# register-loading dot2 kernels (Q4_0 in one- and two-block units), and the
-# matrix-core kernel with activations in LDS and in registers.
+# register-loading dot2 kernels (Q4_0 in one- and two-block units), the
+# matrix-core kernel with activations in LDS and in registers, and the
+# small-problem kernel with and without split-K.
 SCALED_FORMS = [
-    ("q4_0", 1, {"LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
-    ("q4_0", 1, {"LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
-    ("q4_0", 1, {"LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
-    ("q4_0", 2, {"LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
-    ("q4_0", 2, {"LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
-    ("q4_0", 4, {"LQMM_TUNE_GEMV_XREGS": "0"}),
-    ("q4_0", 4, {"LQMM_TUNE_GEMV_XREGS": "1"}),
-    ("q4_k", 1, {"LQMM_TUNE_GEMV_STREAM": "1"}),
-    ("q4_k", 1, {"LQMM_TUNE_GEMV_STREAM": "0"}),
-    ("q4_k", 2, {"LQMM_TUNE_GEMV_STREAM": "1"}),
-    ("q4_k", 2, {"LQMM_TUNE_GEMV_STREAM": "0"}),
-    ("q4_k", 4, {"LQMM_TUNE_GEMV_XREGS": "0"}),
-    ("q4_k", 4, {"LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
+    ("q4_0", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
+    ("q4_0", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "0"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_k", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1"}),
+    ("q4_k", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0"}),
+    ("q4_k", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1"}),
+    ("q4_k", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "0"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "1"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SPLITK": "2"}),
+    ("q4_k", 2, {"LQMM_TUNE_GEMV_SMALL": "1"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SPLITK": "2"}),
 ]
 
 
