@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "LqmmError", "library_path", "load",
-    "lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemm_q8_0_f16", "lqmm_gemv_q4_k",
+    "lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemv_q4_0_noalloc", "lqmm_gemm_q8_0_f16",
+    "lqmm_gemv_q4_k",
     "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version",
     "Q4_0_BLOCK_BYTES", "Q8_0_BLOCK_BYTES", "Q4_K_BLOCK_BYTES",
 ]
@@ -33,8 +34,8 @@ _LIB_PATH = os.path.join(_HERE, "liblqmm.so")
 _lib = None
 
 # Entry points exported by liblqmm.so (the declarations of include/lqmm.h).
-EXPORTS = ("lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemm_q8_0_f16", "lqmm_gemv_q4_k",
-           "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version")
+EXPORTS = ("lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemv_q4_0_noalloc", "lqmm_gemm_q8_0_f16",
+           "lqmm_gemv_q4_k", "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version")
 
 
 class LqmmError(RuntimeError):
@@ -65,6 +66,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
         f.restype = st
+    lib.lqmm_gemv_q4_0_noalloc.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.lqmm_gemv_q4_0_noalloc.restype = st
     lib.lqmm_gemm_q8_0_f16.argtypes = [p, p, p, i64, i64, i64, p]
     lib.lqmm_gemm_q8_0_f16.restype = st
     lib.lqmm_gemv_workspace_bytes.argtypes = [i64, i64, i64]
@@ -213,6 +216,33 @@ def lqmm_gemv_q4_0(W, x, N, out=None, workspace=None, stream=None):
     (zero-filled before first use) for split-K plans; None lets the binding
     provide one per device and stream; False passes none."""
     return _gemv(load().lqmm_gemv_q4_0, 32, Q4_0_BLOCK_BYTES, W, x, N, out, workspace, stream)
+
+
+def lqmm_gemv_q4_0_noalloc(W, x, N, out=None, stream=None):
+    """lqmm_gemv_q4_0 through the allocation-free entry point (split-K plans
+    use the library's static per-GPU scratch; calls on one GPU must not
+    overlap). ``out`` must be given to avoid the binding's own allocation."""
+    torch = _torch()
+    _dev_tensor(W, torch.uint8, "W")
+    _dev_tensor(x, torch.float32, "x")
+    squeeze = x.dim() == 1
+    x2 = x.view(1, -1) if squeeze else x
+    if x2.dim() != 2:
+        raise ValueError("x must be (K,) or (batch, K)")
+    batch, K = x2.shape
+    N = int(N)
+    if K % 32 or W.numel() != N * (K // 32) * Q4_0_BLOCK_BYTES:
+        raise ValueError(f"W holds {W.numel()} bytes, expected N*K/32*18 for N={N}, K={K}")
+    if out is None:
+        out = torch.empty((batch, N), dtype=torch.float32, device=x.device)
+    _dev_tensor(out, torch.float32, "out")
+    if out.numel() != batch * N:
+        raise ValueError("out has the wrong size")
+    _same_device(W, x, out)
+    with torch.cuda.device(x.device):
+        _check(load().lqmm_gemv_q4_0_noalloc(W.data_ptr(), x2.data_ptr(), out.data_ptr(), N, K,
+                                             batch, _stream(stream)))
+    return out.view(-1) if squeeze and out.dim() == 2 and out.shape[0] == 1 else out
 
 
 def lqmm_gemv_q4_k(W, x, N, out=None, workspace=None, stream=None):

@@ -12,15 +12,26 @@
 
 namespace {
 
+// Split-K workspace of the allocation-free GEMV entry point: a static
+// device array, one copy per GPU, zero-initialized when the code object is
+// loaded and kept until the process ends. In host code `scratch` is only a
+// stand-in symbol; its device address on each GPU comes from
+// hipGetSymbolAddress (below) and only that address is ever passed on.
+constexpr size_t kScratchBytes = LQMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 struct DeviceInfo {
   std::once_flag once;
   bool ok = false;
   int num_cus = 0;
+  void *scratch_ptr = nullptr;  // this device's copy of `scratch`
 };
 DeviceInfo g_dev[lqmm::kMaxDevices];
 
-// Current device, checked to be gfx950; CU count cached per device.
-lqmm_status current_device(int *num_cus) {
+// Current device, checked to be gfx950; CU count and the device address of
+// the static scratch array cached per device (set up once, with the device
+// current).
+lqmm_status current_device(int *num_cus, void **scratch_ptr = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= lqmm::kMaxDevices) return LQMM_ERR_DEVICE;
   DeviceInfo &di = g_dev[dev];
@@ -28,11 +39,15 @@ lqmm_status current_device(int *num_cus) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return;
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
+    di.scratch_ptr = p;
     di.num_cus = prop.multiProcessorCount;
     di.ok = di.num_cus > 0;
   });
   if (!di.ok) return LQMM_ERR_DEVICE;
   *num_cus = di.num_cus;
+  if (scratch_ptr) *scratch_ptr = di.scratch_ptr;
   return LQMM_OK;
 }
 
@@ -136,9 +151,12 @@ bool plan_small(lqmm::GemvFormat fmt, int64_t N, int64_t K, int B, int num_cus,
   return true;
 }
 
+// static_ws: ws is the device's static scratch (allocation-free entry
+// point): a split-K plan that needs more than it holds is refused, and the
+// plan's counters are zeroed by a kernel before each split-K launch.
 lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, float *y,
                         int64_t N, int64_t K, int64_t batch, void *ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool static_ws = false) {
   using lqmm::GemvFormat;
   const int blk = fmt == GemvFormat::Q4_0 ? 32 : 256;
   const int blk_bytes = fmt == GemvFormat::Q4_0 ? 18 : 144;
@@ -148,8 +166,13 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   if (ws && !aligned16(ws)) return LQMM_ERR_ALIGN;
 
   int num_cus = 0;
-  lqmm_status st = current_device(&num_cus);
+  void *scratch_ptr = nullptr;
+  lqmm_status st = current_device(&num_cus, &scratch_ptr);
   if (st != LQMM_OK) return st;
+  if (static_ws) {
+    ws = scratch_ptr;
+    ws_bytes = kScratchBytes;
+  }
 
   // Small problems (all rows in passes of at most four): the latency-bound
   // kernel, when its split-K workspace (if it needs one) is there.
@@ -158,7 +181,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     size_t need = 0;
     if (plan_small(fmt, N, K, (int)batch, num_cus, &sp, &need)) {
       if (need > 0 && (!ws || ws_bytes < need)) {
-        if (env_int("LQMM_TUNE_GEMV_SPLITK") > 1) return LQMM_ERR_WORKSPACE;
+        if (static_ws || env_int("LQMM_TUNE_GEMV_SPLITK") > 1) return LQMM_ERR_WORKSPACE;
       } else {
         sp.ldx = K;
         sp.ldy = N;
@@ -166,6 +189,10 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
         float *part = need ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
                                                        align_up((size_t)sp.row_blocks * 4))
                            : nullptr;
+        if (need && static_ws) {
+          hipError_t e = lqmm::gemv_small_clear_counters(cnt, sp.row_blocks, stream);
+          if (e != hipSuccess) return LQMM_ERR_LAUNCH;
+        }
         hipError_t e = lqmm::gemv_small_launch(sp, static_cast<const uint8_t *>(W), x, y, part,
                                                cnt, stream);
         return e == hipSuccess ? LQMM_OK : LQMM_ERR_LAUNCH;
@@ -432,6 +459,12 @@ lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y, int64_t N, i
                            int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
   return gemv_common(lqmm::GemvFormat::Q4_0, W, x, y, N, K, batch, workspace, workspace_bytes,
                      (hipStream_t)stream);
+}
+
+lqmm_status lqmm_gemv_q4_0_noalloc(const void *W, const float *x, float *y, int64_t N,
+                                   int64_t K, int64_t batch, void *stream) {
+  return gemv_common(lqmm::GemvFormat::Q4_0, W, x, y, N, K, batch, nullptr, 0,
+                     (hipStream_t)stream, true);
 }
 
 lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y, int64_t N, int64_t K,

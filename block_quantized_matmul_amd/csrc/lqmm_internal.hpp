@@ -107,6 +107,8 @@ size_t gemv_small_lds_bytes(GemvFormat f, int batch, int nus);
 size_t gemv_small_max_lds();  // the most dynamic LDS a small-kernel plan may use
 hipError_t gemv_small_launch(const SmallGemvPlan &plan, const uint8_t *W, const float *x, float *y,
                              float *partials, int *counters, hipStream_t stream);
+// Zero the first n arrival counters of a workspace (a kernel launch).
+hipError_t gemv_small_clear_counters(int *counters, int n, hipStream_t stream);
 
 // ---- Q8_0 x fp16 GEMM ---------------------------------------------------------
 hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,

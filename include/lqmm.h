@@ -126,6 +126,23 @@ lqmm_status lqmm_gemv_q4_0(const void *W, const float *x, float *y,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lqmm_gemv_q4_0 for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments (without the workspace) and same
+ * results as lqmm_gemv_q4_0 given a workspace. Its split-K plans use a
+ * static device array of LQMM_NOALLOC_SCRATCH_BYTES instead, one per GPU,
+ * held until the process ends; the call itself allocates and frees nothing.
+ * Before each split-K launch it zeroes the plan's arrival counters with a
+ * kernel on `stream`. Every call on a GPU shares that GPU's array, so calls
+ * that may overlap on one GPU (other streams, other threads) race: order
+ * them. A split-K plan needing more scratch than the array holds (possible
+ * only when a tuning override forces one) returns LQMM_ERR_WORKSPACE.
+ */
+#define LQMM_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+lqmm_status lqmm_gemv_q4_0_noalloc(const void *W, const float *x, float *y,
+                                   int64_t N, int64_t K, int64_t batch, void *stream);
+
+/*
  * Q8_0 x fp16 GEMM (prefill): Y[m][n] = sum_k X[m][k] * W[n][k], i.e.
  * Y = X * W^T. W: N x (K/32) Q8_0 blocks; X: M x K fp16; Y: M x N fp16
  * (fp32 accumulation, rounded to nearest even at the end). K % 32 == 0 and
