@@ -50,11 +50,17 @@ class Oracle:
         lib.lqmm_oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.lqmm_oracle_f16_array_to_f64.argtypes = [_p, _p, _i64]
         for name in ("lqmm_oracle_dequant_q4_0", "lqmm_oracle_dequant_q8_0",
-                     "lqmm_oracle_dequant_q4_k"):
+                     "lqmm_oracle_dequant_q4_k", "lqmm_oracle_dequant_q6_k",
+                     "lqmm_oracle_dequant_q2_k"):
             getattr(lib, name).argtypes = [_p, _i64, _i64, _p]
-        for name in ("lqmm_oracle_gemv_q4_0", "lqmm_oracle_gemv_q4_k"):
+        lib.lqmm_oracle_dequant_i4g32.argtypes = [_p, _p, _p, _i64, _i64, _p]
+        for name in ("lqmm_oracle_gemv_q4_0", "lqmm_oracle_gemv_q4_k", "lqmm_oracle_gemv_q8_0",
+                     "lqmm_oracle_gemv_q6_k", "lqmm_oracle_gemv_q2_k"):
             getattr(lib, name).argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
-        lib.lqmm_oracle_gemm_q8_0_f16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
+        lib.lqmm_oracle_gemv_i4g32.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64]
+        for name in ("lqmm_oracle_gemm_q8_0_f16", "lqmm_oracle_gemm_q4_0_f16",
+                     "lqmm_oracle_gemm_q4_k_f16"):
+            getattr(lib, name).argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
         lib.lqmm_oracle_sgemm.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
         lib.lqmm_oracle_mutant.restype = ctypes.c_int
         lib.lqmm_oracle_threads.restype = ctypes.c_int
@@ -97,6 +103,21 @@ class Oracle:
     def dequant_q4_k(self, W, N, K):
         return self._dequant("lqmm_oracle_dequant_q4_k", W, N, K)
 
+    def dequant_q6_k(self, W, N, K):
+        return self._dequant("lqmm_oracle_dequant_q6_k", W, N, K)
+
+    def dequant_q2_k(self, W, N, K):
+        return self._dequant("lqmm_oracle_dequant_q2_k", W, N, K)
+
+    def dequant_i4g32(self, Wq, scales, zeros, N, K):
+        Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
+        sc = np.ascontiguousarray(scales, dtype=np.float32)
+        z = np.ascontiguousarray(zeros, dtype=np.float32)
+        out = np.empty((N, K), np.float64)
+        self.lib.lqmm_oracle_dequant_i4g32(Wq.ctypes.data, sc.ctypes.data, z.ctypes.data, N, K,
+                                           out.ctypes.data)
+        return out
+
     # -- products -----------------------------------------------------------
     @staticmethod
     def _sel(idx):
@@ -124,9 +145,33 @@ class Oracle:
     def gemv_q4_k(self, W, x, N, K, rows=None) -> np.ndarray:
         return self._gemv("lqmm_oracle_gemv_q4_k", W, x, N, K, rows)
 
-    def gemm_q8_0_f16(self, W, X, N, K, cols=None) -> np.ndarray:
-        """Y[m, n] = sum_k X[m, k] W[n, k]; X is fp16 (M, K); returns float64
-        (M, N or len(cols))."""
+    def gemv_q8_0(self, W, x, N, K, rows=None) -> np.ndarray:
+        return self._gemv("lqmm_oracle_gemv_q8_0", W, x, N, K, rows)
+
+    def gemv_q6_k(self, W, x, N, K, rows=None) -> np.ndarray:
+        return self._gemv("lqmm_oracle_gemv_q6_k", W, x, N, K, rows)
+
+    def gemv_q2_k(self, W, x, N, K, rows=None) -> np.ndarray:
+        return self._gemv("lqmm_oracle_gemv_q2_k", W, x, N, K, rows)
+
+    def gemv_i4g32(self, Wq, scales, zeros, x, N, K, rows=None) -> np.ndarray:
+        """The int4 group-32 layout: Wq uint32 words (N*K/8), scales and zeros
+        float32 (N, K/32); returns (batch, N or len(rows))."""
+        Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
+        sc = np.ascontiguousarray(scales, dtype=np.float32)
+        z = np.ascontiguousarray(zeros, dtype=np.float32)
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+        assert x.shape[1] == K
+        b = x.shape[0]
+        keep, nr, rp = self._sel(rows)
+        R = nr if rows is not None else N
+        y = np.empty((b, R), np.float64)
+        self.lib.lqmm_oracle_gemv_i4g32(Wq.ctypes.data, sc.ctypes.data, z.ctypes.data,
+                                        x.ctypes.data, y.ctypes.data, N, K, b, rp, nr)
+        del keep
+        return y
+
+    def _gemm(self, fn, W, X, N, K, cols):
         W = np.ascontiguousarray(W, dtype=np.uint8)
         Xb = np.ascontiguousarray(np.asarray(X, dtype=np.float16)).view(np.uint16)
         M = Xb.shape[0]
@@ -134,10 +179,20 @@ class Oracle:
         keep, nc, cp = self._sel(cols)
         C = nc if cols is not None else N
         Y = np.empty((M, C), np.float64)
-        self.lib.lqmm_oracle_gemm_q8_0_f16(W.ctypes.data, Xb.ctypes.data, Y.ctypes.data,
-                                           M, N, K, cp, nc)
+        getattr(self.lib, fn)(W.ctypes.data, Xb.ctypes.data, Y.ctypes.data, M, N, K, cp, nc)
         del keep
         return Y
+
+    def gemm_q8_0_f16(self, W, X, N, K, cols=None) -> np.ndarray:
+        """Y[m, n] = sum_k X[m, k] W[n, k]; X is fp16 (M, K); returns float64
+        (M, N or len(cols))."""
+        return self._gemm("lqmm_oracle_gemm_q8_0_f16", W, X, N, K, cols)
+
+    def gemm_q4_0_f16(self, W, X, N, K, cols=None) -> np.ndarray:
+        return self._gemm("lqmm_oracle_gemm_q4_0_f16", W, X, N, K, cols)
+
+    def gemm_q4_k_f16(self, W, X, N, K, cols=None) -> np.ndarray:
+        return self._gemm("lqmm_oracle_gemm_q4_k_f16", W, X, N, K, cols)
 
     def sgemm(self, A, B, rows=None) -> np.ndarray:
         """C = A @ B in double; A (M, K) fp32, B (K, N) fp32."""

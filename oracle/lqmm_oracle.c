@@ -40,8 +40,28 @@
  *               m_s  = (scales[s+4] >> 4) | ((scales[s]   >> 6) << 4)
  *     weight l of sub-block s has q = nibble of qs[32*(s/2) + l], low nibble
  *     for even s, high nibble for odd s; w = d * sc_s * q - dmin * m_s.
+ * Further llama.cpp K-quant super-blocks of 256 weights (the pages name the
+ * K-quants and q2_k among the formats; this byte reading is stated once here):
+ *   Q6_K, 210 bytes: ql[128] (low 4 bits of q), qh[64] (high 2 bits),
+ *     int8 scales[16] (one per 16 weights), fp16 d at bytes 208-209;
+ *     w = d * scales[k/16] * (q - 32), q in 0..63. Weight k = 128h + 32j + l
+ *     (h < 2, j < 4, l < 32) takes its low bits from the low (j < 2) or
+ *     high (j >= 2) nibble of ql[64h + l + 32*(j % 2)] and its high bits
+ *     from bits 2j..2j+1 of qh[32h + l].
+ *   Q2_K, 84 bytes: scales[16] (low nibble: scale sc, high nibble: min m,
+ *     one pair per 16 weights), qs[64], fp16 d at bytes 80-81, fp16 dmin at
+ *     bytes 82-83; w = d * sc[k/16] * q - dmin * m[k/16], q in 0..3. Weight
+ *     k = 128h + 32j + l takes bits 2j..2j+1 of qs[32h + l].
  * A weight matrix of N output rows and K inputs stores row n as K/32 (or
  * K/256) consecutive blocks; rows are consecutive with no padding.
+ *
+ * The int4 layout of "Compute Shaders con WebGPU para Inferencia ML",
+ * section "Yendo a Cuantizado: Matmul INT4" (GPTQ/AWQ style): weight (n, k)
+ * is nibble (n*K + k) % 8 (bits 4*i..4*i+3) of 32-bit word (n*K + k) / 8,
+ * read as a two's-complement value s in -8..7; scales and zeros are fp32
+ * arrays of N x K/32 (one per row and group of 32 along K); w = (s - zero)
+ * * scale. (The page's listing does not declare the scales and zeros
+ * buffers; fp32 is the reading its f32 arithmetic supports.)
  *
  * Test hooks: LQMM_ORACLE_MUTANT selects a deliberately wrong variant of one
  * step. It is 0 in every normal build and is only set by the test that checks
@@ -167,6 +187,48 @@ static void deq_q4_k_block(const uint8_t *blk, double *w) {
   }
 }
 
+/* Dequantize one Q6_K super-block (210 bytes) into 256 doubles:
+ * w = d * scales[k/16] * (q - 32). */
+static void deq_q6_k_block(const uint8_t *blk, double *w) {
+  const uint8_t *ql = blk, *qh = blk + 128;
+  const int8_t *sc = (const int8_t *)(blk + 192);
+  double d = lqmm_oracle_f16_to_f64(rd16(blk + 208));
+  for (int k = 0; k < 256; ++k) {
+    int h = k / 128, j = (k % 128) / 32, l = k % 32;
+    uint8_t lb = ql[64 * h + l + 32 * (j % 2)];
+#if LQMM_ORACLE_MUTANT == 12
+    int lo = j < 2 ? (lb >> 4) : (lb & 15); /* nibble halves swapped */
+#else
+    int lo = j < 2 ? (lb & 15) : (lb >> 4);
+#endif
+#if LQMM_ORACLE_MUTANT == 11
+    int hi = (qh[32 * h + l] >> j) & 3; /* high bits at the wrong shift */
+#else
+    int hi = (qh[32 * h + l] >> (2 * j)) & 3;
+#endif
+    int q = lo | (hi << 4);
+    w[k] = d * sc[k / 16] * (q - 32);
+  }
+}
+
+/* Dequantize one Q2_K super-block (84 bytes) into 256 doubles:
+ * w = d * sc * q - dmin * m with (sc, m) the nibbles of scales[k/16]. */
+static void deq_q2_k_block(const uint8_t *blk, double *w) {
+  const uint8_t *scales = blk, *qs = blk + 16;
+  double d = lqmm_oracle_f16_to_f64(rd16(blk + 80));
+  double dmin = lqmm_oracle_f16_to_f64(rd16(blk + 82));
+  for (int k = 0; k < 256; ++k) {
+    int h = k / 128, j = (k % 128) / 32, l = k % 32;
+    int q = (qs[32 * h + l] >> (2 * j)) & 3;
+#if LQMM_ORACLE_MUTANT == 13
+    int m = scales[k / 16] & 15, sc = scales[k / 16] >> 4; /* scale and min swapped */
+#else
+    int sc = scales[k / 16] & 15, m = scales[k / 16] >> 4;
+#endif
+    w[k] = d * sc * q - dmin * m;
+  }
+}
+
 /* ---- dense dequantization of whole rows (exposed for the pins) ---- */
 
 void lqmm_oracle_dequant_q4_0(const uint8_t *W, int64_t N, int64_t K, double *out) {
@@ -190,6 +252,51 @@ void lqmm_oracle_dequant_q4_k(const uint8_t *W, int64_t N, int64_t K, double *ou
       deq_q4_k_block(W + (n * nb + b) * 144, out + n * K + b * QKK);
 }
 
+void lqmm_oracle_dequant_q6_k(const uint8_t *W, int64_t N, int64_t K, double *out) {
+  int64_t nb = K / QKK;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < nb; ++b)
+      deq_q6_k_block(W + (n * nb + b) * 210, out + n * K + b * QKK);
+}
+
+void lqmm_oracle_dequant_q2_k(const uint8_t *W, int64_t N, int64_t K, double *out) {
+  int64_t nb = K / QKK;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < nb; ++b)
+      deq_q2_k_block(W + (n * nb + b) * 84, out + n * K + b * QKK);
+}
+
+/* The int4 group-32 layout ("Yendo a Cuantizado: Matmul INT4"): row n of
+ * N x K, w = (s - zero) * scale with s the sign-extended nibble. */
+static void deq_i4g32_row(const uint32_t *Wq, const float *scales, const float *zeros,
+                          int64_t n, int64_t K, double *w) {
+  for (int64_t k = 0; k < K; ++k) {
+    int64_t idx = n * K + k;
+#if LQMM_ORACLE_MUTANT == 16
+    int nib = (int)((Wq[idx / 8] >> (4 * (7 - idx % 8))) & 15u); /* nibble order reversed */
+#else
+    int nib = (int)((Wq[idx / 8] >> (4 * (idx % 8))) & 15u);
+#endif
+#if LQMM_ORACLE_MUTANT == 14
+    int sv = nib; /* not sign-extended */
+#else
+    int sv = nib >= 8 ? nib - 16 : nib;
+#endif
+    double scale = scales[n * (K / QK) + k / QK];
+    double zero = zeros[n * (K / QK) + k / QK];
+#if LQMM_ORACLE_MUTANT == 15
+    w[k] = (sv + zero) * scale; /* zero point added */
+#else
+    w[k] = (sv - zero) * scale;
+#endif
+  }
+}
+
+void lqmm_oracle_dequant_i4g32(const uint32_t *Wq, const float *scales, const float *zeros,
+                               int64_t N, int64_t K, double *out) {
+  for (int64_t n = 0; n < N; ++n) deq_i4g32_row(Wq, scales, zeros, n, K, out + n * K);
+}
+
 /* ---- GEMV: y[b][n] = sum_k W[n][k] * x[b][k] ----
  * Weight-matrix times activation for decode (one or a few tokens), the
  * mat-vec case of "Llamas na Web", "Design de Shader Consciente de
@@ -210,10 +317,24 @@ static void row_q4_k(const uint8_t *W, int64_t n, int64_t K, double *w) {
   int64_t nb = K / QKK;
   for (int64_t b = 0; b < nb; ++b) deq_q4_k_block(W + (n * nb + b) * 144, w + b * QKK);
 }
+static void row_q6_k(const uint8_t *W, int64_t n, int64_t K, double *w) {
+  int64_t nb = K / QKK;
+  for (int64_t b = 0; b < nb; ++b) deq_q6_k_block(W + (n * nb + b) * 210, w + b * QKK);
+}
+static void row_q2_k(const uint8_t *W, int64_t n, int64_t K, double *w) {
+  int64_t nb = K / QKK;
+  for (int64_t b = 0; b < nb; ++b) deq_q2_k_block(W + (n * nb + b) * 84, w + b * QKK);
+}
 
-static void gemv_generic(deq_row_fn deq, const uint8_t *W, const float *x, double *y,
-                         int64_t N, int64_t K, int64_t batch, const int64_t *rows,
-                         int64_t nrows) {
+/* The int4 layout's three arrays, for gemv_generic's row decoder. */
+typedef struct {
+  const uint32_t *Wq;
+  const float *scales, *zeros;
+} i4g32_arrays;
+
+static void gemv_generic_ex(deq_row_fn deq, const uint8_t *W, const i4g32_arrays *i4,
+                            const float *x, double *y, int64_t N, int64_t K, int64_t batch,
+                            const int64_t *rows, int64_t nrows) {
   int64_t R = rows ? nrows : N;
 #pragma omp parallel
   {
@@ -221,7 +342,10 @@ static void gemv_generic(deq_row_fn deq, const uint8_t *W, const float *x, doubl
 #pragma omp for schedule(static)
     for (int64_t i = 0; i < R; ++i) {
       int64_t n = rows ? rows[i] : i;
-      deq(W, n, K, w);
+      if (i4)
+        deq_i4g32_row(i4->Wq, i4->scales, i4->zeros, n, K, w);
+      else
+        deq(W, n, K, w);
       for (int64_t b = 0; b < batch; ++b) {
         const float *xb = x + b * K;
         double acc = 0.0;
@@ -231,6 +355,12 @@ static void gemv_generic(deq_row_fn deq, const uint8_t *W, const float *x, doubl
     }
     free(w);
   }
+}
+
+static void gemv_generic(deq_row_fn deq, const uint8_t *W, const float *x, double *y,
+                         int64_t N, int64_t K, int64_t batch, const int64_t *rows,
+                         int64_t nrows) {
+  gemv_generic_ex(deq, W, NULL, x, y, N, K, batch, rows, nrows);
 }
 
 void lqmm_oracle_gemv_q4_0(const uint8_t *W, const float *x, double *y, int64_t N,
@@ -243,13 +373,42 @@ void lqmm_oracle_gemv_q4_k(const uint8_t *W, const float *x, double *y, int64_t 
   gemv_generic(row_q4_k, W, x, y, N, K, batch, rows, nrows);
 }
 
-/* ---- Q8_0 x fp16 GEMM: Y[m][n] = sum_k X[m][k] * W[n][k] ----
+/* Decode mat-vec over Q8_0, Q6_K and Q2_K rows: the same definition with the
+ * other block formats (every format takes both kernel styles in "Llamas na
+ * Web", "Design de Shader Consciente de Quantizacao"). */
+void lqmm_oracle_gemv_q8_0(const uint8_t *W, const float *x, double *y, int64_t N,
+                           int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
+  gemv_generic(row_q8_0, W, x, y, N, K, batch, rows, nrows);
+}
+
+void lqmm_oracle_gemv_q6_k(const uint8_t *W, const float *x, double *y, int64_t N,
+                           int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
+  gemv_generic(row_q6_k, W, x, y, N, K, batch, rows, nrows);
+}
+
+void lqmm_oracle_gemv_q2_k(const uint8_t *W, const float *x, double *y, int64_t N,
+                           int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
+  gemv_generic(row_q2_k, W, x, y, N, K, batch, rows, nrows);
+}
+
+/* The int4 matmul of "Yendo a Cuantizado: Matmul INT4": sum over k of
+ * input * (s - zero) * scale, for every weight row and activation row. The
+ * page writes result[row * N + col] with row = weight row and col = input
+ * vector; here y[b][n] (activation-major), the same numbers. */
+void lqmm_oracle_gemv_i4g32(const uint32_t *Wq, const float *scales, const float *zeros,
+                            const float *x, double *y, int64_t N, int64_t K, int64_t batch,
+                            const int64_t *rows, int64_t nrows) {
+  i4g32_arrays a = {Wq, scales, zeros};
+  gemv_generic_ex(NULL, NULL, &a, x, y, N, K, batch, rows, nrows);
+}
+
+/* ---- quantized x fp16 GEMM: Y[m][n] = sum_k X[m][k] * W[n][k] ----
  * The prefill matmul of "Llamas na Web", "Design de Shader Consciente de
  * Quantizacao" (blocks loaded, dequantized and reused). X is M x K raw fp16
  * bits, row-major; Y is M x N double (the unrounded product). cols/ncols
  * select output columns n (cols == NULL: all N); Y is then M x ncols. */
-void lqmm_oracle_gemm_q8_0_f16(const uint8_t *W, const uint16_t *X, double *Y, int64_t M,
-                               int64_t N, int64_t K, const int64_t *cols, int64_t ncols) {
+static void gemm_generic(deq_row_fn deq, const uint8_t *W, const uint16_t *X, double *Y,
+                         int64_t M, int64_t N, int64_t K, const int64_t *cols, int64_t ncols) {
   int64_t C = cols ? ncols : N;
   double *Xd = (double *)malloc(sizeof(double) * (size_t)(M * K));
   for (int64_t i = 0; i < M * K; ++i) Xd[i] = lqmm_oracle_f16_to_f64(X[i]);
@@ -259,7 +418,7 @@ void lqmm_oracle_gemm_q8_0_f16(const uint8_t *W, const uint16_t *X, double *Y, i
 #pragma omp for schedule(static)
     for (int64_t j = 0; j < C; ++j) {
       int64_t n = cols ? cols[j] : j;
-      row_q8_0(W, n, K, w);
+      deq(W, n, K, w);
       for (int64_t m = 0; m < M; ++m) {
         const double *xm = Xd + m * K;
         double acc = 0.0;
@@ -274,6 +433,22 @@ void lqmm_oracle_gemm_q8_0_f16(const uint8_t *W, const uint16_t *X, double *Y, i
     free(w);
   }
   free(Xd);
+}
+
+void lqmm_oracle_gemm_q8_0_f16(const uint8_t *W, const uint16_t *X, double *Y, int64_t M,
+                               int64_t N, int64_t K, const int64_t *cols, int64_t ncols) {
+  gemm_generic(row_q8_0, W, X, Y, M, N, K, cols, ncols);
+}
+
+/* The prefill matmul over Q4_0 and Q4_K weights. */
+void lqmm_oracle_gemm_q4_0_f16(const uint8_t *W, const uint16_t *X, double *Y, int64_t M,
+                               int64_t N, int64_t K, const int64_t *cols, int64_t ncols) {
+  gemm_generic(row_q4_0, W, X, Y, M, N, K, cols, ncols);
+}
+
+void lqmm_oracle_gemm_q4_k_f16(const uint8_t *W, const uint16_t *X, double *Y, int64_t M,
+                               int64_t N, int64_t K, const int64_t *cols, int64_t ncols) {
+  gemm_generic(row_q4_k, W, X, Y, M, N, K, cols, ncols);
 }
 
 /* ---- fp32 GEMM: C[i][j] = sum_k A[i][k] * B[k][j] ----

@@ -105,6 +105,79 @@ def pin_q4_k_worked(o):
         assert o.gemv_q4_k(Wb, _onehot(K, k), 1, K)[0, 0] == float(g[f"b_e{k}"]), k
 
 
+def pin_q8_0_gemv_worked(o):
+    """The Q8_0 worked blocks through the decode GEMV (fp32 activations)."""
+    g = read_golden("q8_0_block.txt")
+    K = 32
+    for blk, keys in (("a", {"ones": None, "e0": 0, "e31": 31}),
+                      ("b", {"ones": None, "e0": 0, "e1": 1})):
+        W = _hex(g[f"{blk}_hex"])
+        for key, k in keys.items():
+            x = np.ones((1, K), np.float32) if k is None else _onehot(K, k)
+            assert o.gemv_q8_0(W, x, 1, K)[0, 0] == float(g[f"{blk}_{key}"]), (blk, key)
+
+
+def pin_gemm_q4_worked(o):
+    """The Q4_0 and Q4_K worked blocks through the prefill GEMMs (fp16 X rows
+    of ones and one-hots are exact)."""
+    g = read_golden("q4_0_block.txt")
+    W = _hex(g["block_hex"])
+    for key, x in {"ones": np.ones((1, 32), np.float32), "e1": _onehot(32, 1),
+                   "e16": _onehot(32, 16), "e31": _onehot(32, 31),
+                   "ramp": np.arange(32, dtype=np.float32)[None]}.items():
+        Y = o.gemm_q4_0_f16(W, x.astype(np.float16), 1, 32)
+        assert Y[0, 0] == float(g[key]), (key, Y[0, 0])
+    gk = read_golden("q4_k_block.txt")
+    Wa = np.concatenate([_hex("003c0038" + gk["scales_hex"]), np.full(128, 0x11, np.uint8)])
+    X = np.zeros((3, 256), np.float16)
+    X[0] = 1
+    X[1, 167] = 1
+    X[2, 128] = 1
+    Y = o.gemm_q4_k_f16(Wa, X, 1, 256)[:, 0]
+    assert list(Y) == [float(gk["a_ones"]), float(gk["a_e167"]), float(gk["a_e128"])], Y
+
+
+def pin_q6_k_worked(o):
+    g = read_golden("q6_k_block.txt")
+    K = 256
+    for blk in ("a", "b"):
+        W = _hex(g[f"{blk}_hex"])
+        assert W.size == 210
+        for key, v in g.items():
+            if not key.startswith(blk + "_") or key.endswith("hex"):
+                continue
+            what = key[2:]
+            x = np.ones((1, K), np.float32) if what == "ones" else _onehot(K, int(what[1:]))
+            assert o.gemv_q6_k(W, x, 1, K)[0, 0] == float(v), (key, o.gemv_q6_k(W, x, 1, K))
+
+
+def pin_q2_k_worked(o):
+    g = read_golden("q2_k_block.txt")
+    K = 256
+    for blk in ("a", "b"):
+        W = _hex(g[f"{blk}_hex"])
+        assert W.size == 84
+        for key, v in g.items():
+            if not key.startswith(blk + "_") or key.endswith("hex"):
+                continue
+            what = key[2:]
+            x = np.ones((1, K), np.float32) if what == "ones" else _onehot(K, int(what[1:]))
+            assert o.gemv_q2_k(W, x, 1, K)[0, 0] == float(v), (key, o.gemv_q2_k(W, x, 1, K))
+
+
+def pin_i4g32_worked(o):
+    g = read_golden("i4g32_block.txt")
+    K = 64
+    Wq = np.frombuffer(bytes.fromhex(g["words_hex"]), dtype="<u4").copy()
+    sc = np.array([[float(v) for v in g["scales"].split()]], np.float32)
+    z = np.array([[float(v) for v in g["zeros"].split()]], np.float32)
+    for key, v in g.items():
+        if key in ("words_hex", "scales", "zeros"):
+            continue
+        x = np.ones((1, K), np.float32) if key == "ones" else _onehot(K, int(key[1:]))
+        assert o.gemv_i4g32(Wq, sc, z, x, 1, K)[0, 0] == float(v), key
+
+
 def pin_packers_match_golden(o):
     """The generator's packers reproduce the hand-worked bytes (so the
     round-trip pins below test the oracle against the stated layout)."""
@@ -124,6 +197,26 @@ def pin_packers_match_golden(o):
     blk = synth.pack_q4_k(np.array([[1.0]], np.float16), np.array([[0.5]], np.float16),
                           sc[None], m[None], qk)
     assert blk.tobytes().hex() == "003c0038" + gk["scales_hex"] + "11" * 128
+    one = np.array([[1.0]], np.float16)
+    k = np.arange(256)
+    g6 = read_golden("q6_k_block.txt")
+    a6 = synth.pack_q6_k(one, (np.arange(16) + 1).astype(np.int8)[None, None],
+                         np.full((1, 256), 33, np.uint8))
+    assert a6.tobytes().hex() == g6["a_hex"]
+    b6 = synth.pack_q6_k(one, np.ones((1, 1, 16), np.int8), (k % 64).astype(np.uint8)[None])
+    assert b6.tobytes().hex() == g6["b_hex"]
+    g2 = read_golden("q2_k_block.txt")
+    gg = np.arange(16)
+    a2 = synth.pack_q2_k(one, np.array([[0.5]], np.float16), gg[None, None], (15 - gg)[None, None],
+                         np.full((1, 256), 3, np.uint8))
+    assert a2.tobytes().hex() == g2["a_hex"]
+    qb = ((k % 32) + (k % 128) // 32) % 4
+    b2 = synth.pack_q2_k(one, np.array([[0.0]], np.float16), np.ones((1, 1, 16)),
+                         np.zeros((1, 1, 16)), qb.astype(np.uint8)[None])
+    assert b2.tobytes().hex() == g2["b_hex"]
+    gi = read_golden("i4g32_block.txt")
+    codes = np.concatenate([np.arange(8), np.arange(-8, 0)] * 4)[None]
+    assert synth.pack_i4g32(codes).astype("<u4").tobytes().hex() == gi["words_hex"]
 
 
 # ---------------------------------------------------------------- round trip
@@ -157,6 +250,31 @@ def pin_round_trip(o):
     # where sc = 0 the weight is -dmin * m whatever q is
     z = ~ok & (dd != 0)
     assert np.array_equal(wk[z], -(dm[z] * mm[z]))
+
+    c6 = synth.q6_k_case(9, 512, seed=31)
+    w6 = o.dequant_q6_k(c6.W, c6.N, c6.K)
+    ds = (np.repeat(c6.d.astype(np.float64), 256, axis=1)
+          * np.repeat(c6.sc.reshape(c6.N, -1).astype(np.float64), 16, axis=1))
+    nz = ds != 0
+    assert np.array_equal(w6[nz] / ds[nz] + 32, c6.q.astype(np.float64)[nz])
+
+    c2 = synth.q2_k_case(9, 512, seed=32)
+    w2 = o.dequant_q2_k(c2.W, c2.N, c2.K)
+    d2 = np.repeat(c2.d.astype(np.float64), 256, axis=1)
+    m2 = np.repeat(c2.dmin.astype(np.float64), 256, axis=1)
+    s2 = np.repeat(c2.sc.reshape(c2.N, -1).astype(np.float64), 16, axis=1)
+    mm2 = np.repeat(c2.m.reshape(c2.N, -1).astype(np.float64), 16, axis=1)
+    ok2 = (d2 * s2) != 0
+    q2rec = (w2[ok2] + m2[ok2] * mm2[ok2]) / (d2[ok2] * s2[ok2])
+    assert np.array_equal(np.rint(q2rec), c2.q.astype(np.float64)[ok2])
+    assert np.allclose(q2rec, c2.q.astype(np.float64)[ok2], rtol=0, atol=1e-9)
+
+    ci = synth.i4g32_case(7, 128, seed=33)
+    wi = o.dequant_i4g32(ci.Wq, ci.scales, ci.zeros, ci.N, ci.K)
+    scl = np.repeat(ci.scales.astype(np.float64), 32, axis=1)
+    zr = np.repeat(ci.zeros.astype(np.float64), 32, axis=1)
+    nz = scl != 0
+    assert np.array_equal(wi[nz] / scl[nz] + zr[nz], ci.s.astype(np.float64)[nz])
 
 
 # --------------------------------------------------- closed forms, invariants
@@ -222,6 +340,52 @@ def pin_closed_forms_gemm(o):
     assert np.array_equal(o.gemm_q8_0_f16(c.W, c.X, c.N, c.K, cols=cols), full[:, cols])
 
 
+def pin_closed_forms_new_formats(o):
+    """x = ones gives integer-sum closed forms; one-hot x (or one-hot X rows
+    for the GEMMs) gives a column, rebuilt from the generator's fields."""
+    c8 = synth.q8_0_gemv_case(7, 160, seed=41)
+    y = o.gemv_q8_0(c8.W, np.ones((1, c8.K), np.float32), c8.N, c8.K)[0]
+    ref = (c8.d.astype(np.float64) * c8.q.reshape(c8.N, -1, 32).astype(np.int64).sum(-1)).sum(-1)
+    assert np.allclose(y, ref, rtol=1e-13, atol=0)
+    col = o.gemv_q8_0(c8.W, _onehot(c8.K, 77), c8.N, c8.K)[0]
+    assert np.array_equal(col, c8.d[:, 2].astype(np.float64) * c8.q[:, 77])
+
+    g0 = synth.q4_0_gemm_case(3, 6, 128, seed=42)
+    X = np.zeros((2, g0.K), np.float16)
+    X[0, 45] = 1
+    X[1] = 1
+    Y = o.gemm_q4_0_f16(g0.W, X, g0.N, g0.K)
+    w = g0.w
+    assert np.array_equal(Y[0], w.d[:, 1].astype(np.float64) * (w.q[:, 45].astype(np.float64) - 8))
+    qs = w.q.reshape(w.N, -1, 32).astype(np.int64).sum(-1) - 256
+    assert np.allclose(Y[1], (w.d.astype(np.float64) * qs).sum(-1), rtol=1e-13, atol=0)
+
+    gk = synth.q4_k_gemm_case(2, 5, 512, seed=43)
+    wk = gk.w
+    X = np.zeros((1, gk.K), np.float16)
+    X[0, 300] = 1
+    Y = o.gemm_q4_k_f16(gk.W, X, gk.N, gk.K)[0]
+    ref = (wk.d[:, 1].astype(np.float64) * wk.sc[:, 1, 1] * wk.q[:, 300]
+           - wk.dmin[:, 1].astype(np.float64) * wk.m[:, 1, 1])
+    assert np.array_equal(Y, ref)
+
+    c6 = synth.q6_k_case(5, 256, seed=44)
+    for k in (0, 47, 130, 255):
+        col = o.gemv_q6_k(c6.W, _onehot(256, k), c6.N, 256)[0]
+        ref = c6.d[:, 0].astype(np.float64) * c6.sc[:, 0, k // 16] * (c6.q[:, k].astype(np.int64) - 32)
+        assert np.array_equal(col, ref), k
+    c2 = synth.q2_k_case(5, 256, seed=45)
+    y = o.gemv_q2_k(c2.W, np.ones((1, 256), np.float32), c2.N, 256)[0]
+    qsum = c2.q.reshape(c2.N, 16, 16).astype(np.int64).sum(-1)
+    ref = (c2.d[:, :1].astype(np.float64) * (c2.sc[:, 0] * qsum).sum(-1, keepdims=True)
+           - 16 * c2.dmin[:, :1].astype(np.float64) * c2.m[:, 0].sum(-1, keepdims=True))[:, 0]
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+    ci = synth.i4g32_case(4, 64, seed=46)
+    col = o.gemv_i4g32(ci.Wq, ci.scales, ci.zeros, _onehot(64, 50), ci.N, 64)[0]
+    ref = (ci.s[:, 50].astype(np.float64) - ci.zeros[:, 1]) * ci.scales[:, 1].astype(np.float64)
+    assert np.array_equal(col, ref)
+
+
 def pin_sgemm_identity(o):
     rng = np.random.default_rng(12)
     A = rng.uniform(-1, 1, (7, 5)).astype(np.float32)
@@ -260,6 +424,44 @@ def pin_numpy_crosscheck(o):
     ref8 = c8.X.astype(np.float64) @ W8.T
     Y8 = o.gemm_q8_0_f16(c8.W, c8.X, c8.N, c8.K)
     assert np.allclose(Y8, ref8, rtol=1e-12, atol=1e-12 * np.abs(ref8).max())
+
+    def close(got, ref):
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+    q8 = synth.q8_0_gemv_case(20, 512, batch=3, seed=17)
+    W8v = q8.d.astype(np.float64).repeat(32, axis=1) * q8.q.astype(np.float64)
+    close(o.gemv_q8_0(q8.W, q8.x, q8.N, q8.K), q8.x.astype(np.float64) @ W8v.T)
+
+    g0 = synth.q4_0_gemm_case(9, 17, 256, seed=18)
+    W0 = g0.w.d.astype(np.float64).repeat(32, axis=1) * (g0.w.q.astype(np.float64) - 8)
+    close(o.gemm_q4_0_f16(g0.W, g0.X, g0.N, g0.K), g0.X.astype(np.float64) @ W0.T)
+
+    gk = synth.q4_k_gemm_case(9, 11, 512, seed=19)
+    w = gk.w
+    n, nsb = w.N, w.K // 256
+    Wg = (np.repeat(w.d.astype(np.float64), 256, axis=1)
+          * np.repeat(w.sc.reshape(n, nsb * 8).astype(np.float64), 32, axis=1) * w.q
+          - np.repeat(w.dmin.astype(np.float64), 256, axis=1)
+          * np.repeat(w.m.reshape(n, nsb * 8).astype(np.float64), 32, axis=1))
+    close(o.gemm_q4_k_f16(gk.W, gk.X, gk.N, gk.K), gk.X.astype(np.float64) @ Wg.T)
+
+    c6 = synth.q6_k_case(13, 512, batch=2, seed=20)
+    W6 = (np.repeat(c6.d.astype(np.float64), 256, axis=1)
+          * np.repeat(c6.sc.reshape(c6.N, -1).astype(np.float64), 16, axis=1)
+          * (c6.q.astype(np.float64) - 32))
+    close(o.gemv_q6_k(c6.W, c6.x, c6.N, c6.K), c6.x.astype(np.float64) @ W6.T)
+
+    c2 = synth.q2_k_case(13, 512, batch=2, seed=25)
+    W2 = (np.repeat(c2.d.astype(np.float64), 256, axis=1)
+          * np.repeat(c2.sc.reshape(c2.N, -1).astype(np.float64), 16, axis=1) * c2.q
+          - np.repeat(c2.dmin.astype(np.float64), 256, axis=1)
+          * np.repeat(c2.m.reshape(c2.N, -1).astype(np.float64), 16, axis=1))
+    close(o.gemv_q2_k(c2.W, c2.x, c2.N, c2.K), c2.x.astype(np.float64) @ W2.T)
+
+    ci = synth.i4g32_case(13, 256, batch=2, seed=26)
+    Wi = ((ci.s.astype(np.float64) - np.repeat(ci.zeros.astype(np.float64), 32, axis=1))
+          * np.repeat(ci.scales.astype(np.float64), 32, axis=1))
+    close(o.gemv_i4g32(ci.Wq, ci.scales, ci.zeros, ci.x, ci.N, ci.K), ci.x.astype(np.float64) @ Wi.T)
 
     s = synth.sgemm_case(33, 47, 129, seed=16)
     refs = s.A.astype(np.float64) @ s.B.astype(np.float64)
@@ -301,6 +503,41 @@ def pin_brute_force(o):
             ex = sum(_F(c8.X[m, k]) * _F(c8.d[n, k // 32]) * int(c8.q[n, k]) for k in range(c8.K))
             assert abs(Fraction(Y8[m, n]) - ex) <= Fraction(1, 10**12) * max(abs(ex), Fraction(1, 10**6))
 
+    def exact_ok(got, ex):
+        assert abs(Fraction(got) - ex) <= Fraction(1, 10**12) * max(abs(ex), Fraction(1, 10**6))
+
+    c6 = synth.q6_k_case(2, 256, batch=1, seed=27)
+    y6 = o.gemv_q6_k(c6.W, c6.x, c6.N, c6.K)
+    for n in range(c6.N):
+        exact_ok(y6[0, n], sum(_F(c6.d[n, 0]) * int(c6.sc[n, 0, k // 16]) * (int(c6.q[n, k]) - 32)
+                               * _F(c6.x[0, k]) for k in range(256)))
+    c2 = synth.q2_k_case(2, 256, batch=1, seed=28)
+    y2 = o.gemv_q2_k(c2.W, c2.x, c2.N, c2.K)
+    for n in range(c2.N):
+        exact_ok(y2[0, n], sum((_F(c2.d[n, 0]) * int(c2.sc[n, 0, k // 16]) * int(c2.q[n, k])
+                                - _F(c2.dmin[n, 0]) * int(c2.m[n, 0, k // 16])) * _F(c2.x[0, k])
+                               for k in range(256)))
+    ci = synth.i4g32_case(2, 64, batch=2, seed=29)
+    yi = o.gemv_i4g32(ci.Wq, ci.scales, ci.zeros, ci.x, ci.N, ci.K)
+    for b in range(2):
+        for n in range(ci.N):
+            exact_ok(yi[b, n], sum((int(ci.s[n, k]) - _F(ci.zeros[n, k // 32]))
+                                   * _F(ci.scales[n, k // 32]) * _F(ci.x[b, k]) for k in range(64)))
+    q8 = synth.q8_0_gemv_case(2, 64, batch=1, seed=30)
+    y8 = o.gemv_q8_0(q8.W, q8.x, q8.N, q8.K)
+    for n in range(q8.N):
+        exact_ok(y8[0, n], sum(_F(q8.d[n, k // 32]) * int(q8.q[n, k]) * _F(q8.x[0, k])
+                               for k in range(64)))
+    gk = synth.q4_k_gemm_case(2, 2, 256, seed=34)
+    Yk = o.gemm_q4_k_f16(gk.W, gk.X, gk.N, gk.K)
+    w = gk.w
+    for m in range(2):
+        for n in range(2):
+            exact_ok(Yk[m, n], sum(_F(gk.X[m, k]) * (_F(w.d[n, 0]) * int(w.sc[n, 0, k // 32])
+                                                      * int(w.q[n, k])
+                                                      - _F(w.dmin[n, 0]) * int(w.m[n, 0, k // 32]))
+                                   for k in range(256)))
+
     s = synth.sgemm_case(3, 5, 7, seed=24)
     Cs = o.sgemm(s.A, s.B)
     for i in range(3):
@@ -320,6 +557,7 @@ def pin_subnormal_scales(o):
 
 
 PINS = [pin_f16_exhaustive, pin_q4_0_worked, pin_q8_0_worked, pin_q4_k_worked,
-        pin_packers_match_golden, pin_round_trip, pin_closed_forms_q4_0,
-        pin_closed_forms_q4_k, pin_closed_forms_gemm, pin_sgemm_identity,
-        pin_numpy_crosscheck, pin_brute_force, pin_subnormal_scales]
+        pin_q8_0_gemv_worked, pin_gemm_q4_worked, pin_q6_k_worked, pin_q2_k_worked,
+        pin_i4g32_worked, pin_packers_match_golden, pin_round_trip, pin_closed_forms_q4_0,
+        pin_closed_forms_q4_k, pin_closed_forms_gemm, pin_closed_forms_new_formats,
+        pin_sgemm_identity, pin_numpy_crosscheck, pin_brute_force, pin_subnormal_scales]

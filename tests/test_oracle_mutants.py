@@ -22,7 +22,13 @@ MUTANTS = {
     7: "fp16 subnormals decoded as normals",
     8: "fp16 exponent bias off by one",
     9: "fp32 GEMM reads B transposed",
-    10: "Q8_0 GEMM k index scrambled",
+    10: "quantized GEMM k index scrambled",
+    11: "Q6_K high bits at the wrong shift",
+    12: "Q6_K low-bit nibble halves swapped",
+    13: "Q2_K scale and min nibbles swapped",
+    14: "int4 codes not sign-extended",
+    15: "int4 zero point added instead of subtracted",
+    16: "int4 nibble order reversed within a word",
 }
 
 
