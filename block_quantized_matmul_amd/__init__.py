@@ -20,14 +20,18 @@ import os
 __all__ = [
     "LqmmError", "library_path", "load",
     "lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemv_q4_0_noalloc", "lqmm_gemm_q8_0_f16",
-    "lqmm_gemv_q4_k",
+    "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k", "lqmm_gemv_q2_k", "lqmm_gemv_i4g32",
+    "lqmm_gemm_q4_0_f16", "lqmm_gemm_q4_k_f16",
     "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version",
-    "Q4_0_BLOCK_BYTES", "Q8_0_BLOCK_BYTES", "Q4_K_BLOCK_BYTES",
+    "Q4_0_BLOCK_BYTES", "Q8_0_BLOCK_BYTES", "Q4_K_BLOCK_BYTES", "Q6_K_BLOCK_BYTES",
+    "Q2_K_BLOCK_BYTES",
 ]
 
 Q4_0_BLOCK_BYTES = 18   # 32 weights
 Q8_0_BLOCK_BYTES = 34   # 32 weights
 Q4_K_BLOCK_BYTES = 144  # 256 weights
+Q6_K_BLOCK_BYTES = 210  # 256 weights
+Q2_K_BLOCK_BYTES = 84   # 256 weights
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblqmm.so")
@@ -35,7 +39,9 @@ _lib = None
 
 # Entry points exported by liblqmm.so (the declarations of include/lqmm.h).
 EXPORTS = ("lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemv_q4_0_noalloc", "lqmm_gemm_q8_0_f16",
-           "lqmm_gemv_q4_k", "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version")
+           "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k", "lqmm_gemv_q2_k",
+           "lqmm_gemv_i4g32", "lqmm_gemm_q4_0_f16", "lqmm_gemm_q4_k_f16",
+           "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version")
 
 
 class LqmmError(RuntimeError):
@@ -62,9 +68,16 @@ def load():
     st = ctypes.c_int
     lib.lqmm_sgemm.argtypes = [p, p, p, i64, i64, i64, p]
     lib.lqmm_sgemm.restype = st
-    for name in ("lqmm_gemv_q4_0", "lqmm_gemv_q4_k"):
+    for name in ("lqmm_gemv_q4_0", "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k",
+                 "lqmm_gemv_q2_k"):
         f = getattr(lib, name)
         f.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
+        f.restype = st
+    lib.lqmm_gemv_i4g32.argtypes = [p, p, p, p, p, i64, i64, i64, p, sz, p]
+    lib.lqmm_gemv_i4g32.restype = st
+    for name in ("lqmm_gemm_q4_0_f16", "lqmm_gemm_q4_k_f16"):
+        f = getattr(lib, name)
+        f.argtypes = [p, p, p, i64, i64, i64, p]
         f.restype = st
     lib.lqmm_gemv_q4_0_noalloc.argtypes = [p, p, p, i64, i64, i64, p]
     lib.lqmm_gemv_q4_0_noalloc.restype = st
@@ -250,9 +263,7 @@ def lqmm_gemv_q4_k(W, x, N, out=None, workspace=None, stream=None):
     return _gemv(load().lqmm_gemv_q4_k, 256, Q4_K_BLOCK_BYTES, W, x, N, out, workspace, stream)
 
 
-def lqmm_gemm_q8_0_f16(W, X, N, out=None, stream=None):
-    """Y = X @ W^T: X (M, K) fp16, W an N x K matrix of Q8_0 blocks ->
-    Y (M, N) fp16 (fp32 accumulation)."""
+def _gemm(fn, blk, blk_bytes, W, X, N, out, stream):
     torch = _torch()
     _dev_tensor(W, torch.uint8, "W")
     _dev_tensor(X, torch.float16, "X")
@@ -260,8 +271,9 @@ def lqmm_gemm_q8_0_f16(W, X, N, out=None, stream=None):
         raise ValueError("X must be (M, K)")
     M, K = X.shape
     N = int(N)
-    if K % 32 or W.numel() != N * (K // 32) * Q8_0_BLOCK_BYTES:
-        raise ValueError(f"W holds {W.numel()} bytes, expected N*K/32*34 for N={N}, K={K}")
+    if K % blk or W.numel() != N * (K // blk) * blk_bytes:
+        raise ValueError(f"W holds {W.numel()} bytes, expected N*K/{blk}*{blk_bytes} "
+                         f"for N={N}, K={K}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=X.device)
     _dev_tensor(out, torch.float16, "out")
@@ -269,6 +281,78 @@ def lqmm_gemm_q8_0_f16(W, X, N, out=None, stream=None):
         raise ValueError("out has the wrong shape")
     _same_device(W, X, out)
     with torch.cuda.device(X.device):
-        _check(load().lqmm_gemm_q8_0_f16(W.data_ptr(), X.data_ptr(), out.data_ptr(), M, N, K,
-                                         _stream(stream)))
+        _check(fn(W.data_ptr(), X.data_ptr(), out.data_ptr(), M, N, K, _stream(stream)))
     return out
+
+
+def lqmm_gemm_q8_0_f16(W, X, N, out=None, stream=None):
+    """Y = X @ W^T: X (M, K) fp16, W an N x K matrix of Q8_0 blocks ->
+    Y (M, N) fp16 (fp32 accumulation)."""
+    return _gemm(load().lqmm_gemm_q8_0_f16, 32, Q8_0_BLOCK_BYTES, W, X, N, out, stream)
+
+
+def lqmm_gemm_q4_0_f16(W, X, N, out=None, stream=None):
+    """Y = X @ W^T with W an N x K matrix of Q4_0 blocks (prefill)."""
+    return _gemm(load().lqmm_gemm_q4_0_f16, 32, Q4_0_BLOCK_BYTES, W, X, N, out, stream)
+
+
+def lqmm_gemm_q4_k_f16(W, X, N, out=None, stream=None):
+    """Y = X @ W^T with W an N x K matrix of Q4_K super-blocks (prefill)."""
+    return _gemm(load().lqmm_gemm_q4_k_f16, 256, Q4_K_BLOCK_BYTES, W, X, N, out, stream)
+
+
+def lqmm_gemv_q8_0(W, x, N, out=None, workspace=None, stream=None):
+    """y = x @ W^T with W an N x K matrix of Q8_0 blocks (decode)."""
+    return _gemv(load().lqmm_gemv_q8_0, 32, Q8_0_BLOCK_BYTES, W, x, N, out, workspace, stream)
+
+
+def lqmm_gemv_q6_k(W, x, N, out=None, workspace=None, stream=None):
+    """y = x @ W^T with W an N x K matrix of Q6_K super-blocks (decode)."""
+    return _gemv(load().lqmm_gemv_q6_k, 256, Q6_K_BLOCK_BYTES, W, x, N, out, workspace, stream)
+
+
+def lqmm_gemv_q2_k(W, x, N, out=None, workspace=None, stream=None):
+    """y = x @ W^T with W an N x K matrix of Q2_K super-blocks (decode)."""
+    return _gemv(load().lqmm_gemv_q2_k, 256, Q2_K_BLOCK_BYTES, W, x, N, out, workspace, stream)
+
+
+def lqmm_gemv_i4g32(Wq, scales, zeros, x, N, out=None, workspace=None, stream=None):
+    """y = x @ W^T for the int4 group-32 layout: Wq int32/uint32-packed codes
+    (N*K/8 words, as a torch.int32 tensor), scales and zeros float32
+    (N, K/32)."""
+    torch = _torch()
+    _dev_tensor(Wq, torch.int32, "Wq")
+    _dev_tensor(scales, torch.float32, "scales")
+    _dev_tensor(zeros, torch.float32, "zeros")
+    _dev_tensor(x, torch.float32, "x")
+    squeeze = x.dim() == 1
+    x2 = x.view(1, -1) if squeeze else x
+    if x2.dim() != 2:
+        raise ValueError("x must be (K,) or (batch, K)")
+    batch, K = x2.shape
+    N = int(N)
+    if K % 32 or Wq.numel() != N * K // 8 or scales.numel() != N * K // 32 \
+            or zeros.numel() != N * K // 32:
+        raise ValueError(f"int4 arrays do not match N={N}, K={K}")
+    if out is None:
+        out = torch.empty((batch, N), dtype=torch.float32, device=x.device)
+    _dev_tensor(out, torch.float32, "out")
+    if out.numel() != batch * N:
+        raise ValueError("out has the wrong size")
+    _same_device(Wq, scales, zeros, x, out)
+    ws_ptr, ws_bytes = None, 0
+    with torch.cuda.device(x.device):
+        st = _stream(stream)
+        if workspace is None:
+            need = load().lqmm_gemv_workspace_bytes(N, K, batch)
+            if need:
+                workspace = _default_workspace(x.device, st, need)
+        elif workspace is False:
+            workspace = None
+        if workspace is not None:
+            _dev_tensor(workspace, torch.uint8, "workspace")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+        _check(load().lqmm_gemv_i4g32(Wq.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                      x2.data_ptr(), out.data_ptr(), N, K, batch, ws_ptr,
+                                      ws_bytes, st))
+    return out.view(-1) if squeeze and out.dim() == 2 and out.shape[0] == 1 else out

@@ -82,6 +82,28 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 // workgroup: the most (4, 2, 1) that still give every CU a workgroup.
 // Returns false when the problem is not small (or the override disables the
 // kernel); the workspace the plan needs is *ws_need (0 for one slice).
+// Formats that run on the small-problem kernel only (at any size).
+bool small_only(lqmm::GemvFormat f) {
+  using lqmm::GemvFormat;
+  return f == GemvFormat::Q8_0 || f == GemvFormat::Q6_K || f == GemvFormat::Q2_K ||
+         f == GemvFormat::I4G32;
+}
+
+// Bytes per row of N x K weights in format f.
+int64_t gemv_row_bytes(lqmm::GemvFormat f, int64_t K) {
+  using lqmm::GemvFormat;
+  switch (f) {
+    case GemvFormat::Q4_0:
+    case GemvFormat::Q4_0x2: return K / 32 * 18;
+    case GemvFormat::Q4_K: return K / 256 * 144;
+    case GemvFormat::Q8_0: return K / 32 * 34;
+    case GemvFormat::Q6_K: return K / 256 * 210;
+    case GemvFormat::Q2_K: return K / 256 * 84;
+    case GemvFormat::I4G32: return K / 2;
+  }
+  return 0;
+}
+
 bool plan_small(lqmm::GemvFormat fmt, int64_t N, int64_t K, int B, int num_cus,
                 lqmm::SmallGemvPlan *pl, size_t *ws_need) {
   using lqmm::GemvFormat;
@@ -89,15 +111,22 @@ bool plan_small(lqmm::GemvFormat fmt, int64_t N, int64_t K, int B, int num_cus,
   const int env_splitk = env_int("LQMM_TUNE_GEMV_SPLITK");
   const int env_u = env_int("LQMM_TUNE_GEMV_SMALL_U");
   const int env_nw = env_int("LQMM_TUNE_GEMV_SMALL_WAVES");
-  if (env_small == 0 || B < 1 || B > (env_small == 1 ? kSmallMaxBatch : kSmallBatch)) return false;
+  const bool only = small_only(fmt);
+  if (!only && (env_small == 0 || B > (env_small == 1 ? kSmallMaxBatch : kSmallBatch)))
+    return false;
+  if (B < 1 || B > kSmallMaxBatch) return false;
   const GemvFormat f = fmt == GemvFormat::Q4_0 && K % 64 == 0 ? GemvFormat::Q4_0x2 : fmt;
   const int uw = lqmm::gemv_unit_weights(f);
   const int64_t nu64 = K / uw;
-  if (env_small != 1 && N * (K / 64) > kSmallMaxUnits) return false;
+  if (!only && env_small != 1 && N * (K / 64) > kSmallMaxUnits) return false;
   if (nu64 > (1 << 24)) return false;
   const int nu = (int)nu64;
-  const int U = env_u == 2 ? 2 : 1;
-  const int step = f == GemvFormat::Q4_K ? 4 : 1;  // Q4_K slices start on super-blocks
+  // slices start on super-blocks: Q4_K (4 units each), Q6_K and Q2_K (2)
+  const int step = f == GemvFormat::Q4_K ? 4 : (f == GemvFormat::Q6_K || f == GemvFormat::Q2_K) ? 2 : 1;
+  // Units per lane: one; for the formats that run here at any size, two when
+  // that saves a split-K pass over a large matrix (4 * num_cus rows or more).
+  int U = env_u == 2 ? 2 : 1;
+  if (env_u != 1 && env_u != 2 && only && nu > 64 && nu <= 128 && N >= 4 * (int64_t)num_cus) U = 2;
   auto slice_units = [&](int S) {
     int n = (nu + S - 1) / S;
     return (n + step - 1) / step * step;
@@ -121,7 +150,7 @@ bool plan_small(lqmm::GemvFormat fmt, int64_t N, int64_t K, int B, int num_cus,
   // sixteen-wave 5.15; 1024 x 1024 with 256 one-wave workgroups 3.9-4.2 us,
   // 64 four-wave 3.66, 32 eight-wave 3.75. 8 and 16 waves for one unit per
   // lane at one or two rows.
-  const bool wide = U == 1 && B <= 2;
+  const bool wide = B <= 2;
   int nw = 1;
   for (int c : {16, 8, 4, 2}) {
     if ((c <= 4 || wide) && blocks(c) * S * 4 >= num_cus) {
@@ -144,7 +173,7 @@ bool plan_small(lqmm::GemvFormat fmt, int64_t N, int64_t K, int B, int num_cus,
   pl->row_blocks = (int)rb;
   pl->grid = (int)(rb * S);
   pl->lds_bytes = lds;
-  pl->row_bytes = f == GemvFormat::Q4_K ? K / 256 * 144 : K / 32 * 18;
+  pl->row_bytes = gemv_row_bytes(f, K);
   pl->N = N;
   // counters (one int per row block), then S * B * N partial sums
   *ws_need = S == 1 ? 0 : align_up((size_t)rb * 4) + (size_t)S * B * (size_t)N * 4;
@@ -439,6 +468,43 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   return LQMM_OK;
 }
 
+// GEMV over the formats that run on the small-problem kernel only: passes of
+// up to four activation rows; split-K plans (rows longer than one wave's
+// slice) need the workspace.
+lqmm_status gemv_more(lqmm::GemvFormat f, int blk, const void *W, const float *aux_a,
+                      const float *aux_b, const float *x, float *y, int64_t N, int64_t K,
+                      int64_t batch, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!W || !x || !y) return LQMM_ERR_NULL;
+  if (f == lqmm::GemvFormat::I4G32 && (!aux_a || !aux_b)) return LQMM_ERR_NULL;
+  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(batch) || K % blk != 0) return LQMM_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(x) || !aligned16(y)) return LQMM_ERR_ALIGN;
+  if (aux_a && (!aligned16(aux_a) || !aligned16(aux_b))) return LQMM_ERR_ALIGN;
+  if (ws && !aligned16(ws)) return LQMM_ERR_ALIGN;
+  int num_cus = 0;
+  lqmm_status st = current_device(&num_cus);
+  if (st != LQMM_OK) return st;
+  for (int64_t b0 = 0; b0 < batch; b0 += kSmallMaxBatch) {
+    const int B = (int)(batch - b0 < kSmallMaxBatch ? batch - b0 : kSmallMaxBatch);
+    lqmm::SmallGemvPlan sp;
+    size_t need = 0;
+    if (!plan_small(f, N, K, B, num_cus, &sp, &need)) return LQMM_ERR_SHAPE;
+    if (need > 0 && (!ws || ws_bytes < need)) return LQMM_ERR_WORKSPACE;
+    sp.ldx = K;
+    sp.ldy = N;
+    sp.aux_a = aux_a;
+    sp.aux_b = aux_b;
+    sp.aux_groups = K / 32;
+    int *cnt = need ? static_cast<int *>(ws) : nullptr;
+    float *part = need ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                   align_up((size_t)sp.row_blocks * 4))
+                       : nullptr;
+    hipError_t e = lqmm::gemv_small_launch(sp, static_cast<const uint8_t *>(W), x + b0 * K,
+                                           y + b0 * N, part, cnt, stream);
+    if (e != hipSuccess) return LQMM_ERR_LAUNCH;
+  }
+  return LQMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -473,6 +539,31 @@ lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y, int64_t N, i
                      (hipStream_t)stream);
 }
 
+lqmm_status lqmm_gemv_q8_0(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                           int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
+  return gemv_more(lqmm::GemvFormat::Q8_0, 32, W, nullptr, nullptr, x, y, N, K, batch, workspace,
+                   workspace_bytes, (hipStream_t)stream);
+}
+
+lqmm_status lqmm_gemv_q6_k(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                           int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
+  return gemv_more(lqmm::GemvFormat::Q6_K, 256, W, nullptr, nullptr, x, y, N, K, batch, workspace,
+                   workspace_bytes, (hipStream_t)stream);
+}
+
+lqmm_status lqmm_gemv_q2_k(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                           int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
+  return gemv_more(lqmm::GemvFormat::Q2_K, 256, W, nullptr, nullptr, x, y, N, K, batch, workspace,
+                   workspace_bytes, (hipStream_t)stream);
+}
+
+lqmm_status lqmm_gemv_i4g32(const uint32_t *Wq, const float *scales, const float *zeros,
+                            const float *x, float *y, int64_t N, int64_t K, int64_t batch,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  return gemv_more(lqmm::GemvFormat::I4G32, 32, Wq, scales, zeros, x, y, N, K, batch, workspace,
+                   workspace_bytes, (hipStream_t)stream);
+}
+
 lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, int64_t M,
                                int64_t N, int64_t K, void *stream) {
   if (!W || !X || !Y) return LQMM_ERR_NULL;
@@ -487,16 +578,46 @@ lqmm_status lqmm_gemm_q8_0_f16(const void *W, const uint16_t *X, uint16_t *Y, in
   return e == hipSuccess ? LQMM_OK : LQMM_ERR_LAUNCH;
 }
 
+static lqmm_status gemm_lds_common(lqmm::GemmFormat f, int blk, const void *W, const uint16_t *X,
+                                   uint16_t *Y, int64_t M, int64_t N, int64_t K, void *stream) {
+  if (!W || !X || !Y) return LQMM_ERR_NULL;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || K % blk != 0) return LQMM_ERR_SHAPE;
+  if (K >= LQMM_GEMM_MAX_K) return LQMM_ERR_SHAPE;  // 31-bit load offsets within a tile
+  if (!aligned16(W) || !aligned16(X) || !aligned16(Y)) return LQMM_ERR_ALIGN;
+  int num_cus = 0;
+  lqmm_status st = current_device(&num_cus);
+  if (st != LQMM_OK) return st;
+  hipError_t e = lqmm::gemm_lds_launch(f, static_cast<const uint8_t *>(W), X, Y, M, N, K,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? LQMM_OK : LQMM_ERR_LAUNCH;
+}
+
+lqmm_status lqmm_gemm_q4_0_f16(const void *W, const uint16_t *X, uint16_t *Y, int64_t M,
+                               int64_t N, int64_t K, void *stream) {
+  return gemm_lds_common(lqmm::GemmFormat::Q4_0, 32, W, X, Y, M, N, K, stream);
+}
+
+lqmm_status lqmm_gemm_q4_k_f16(const void *W, const uint16_t *X, uint16_t *Y, int64_t M,
+                               int64_t N, int64_t K, void *stream) {
+  return gemm_lds_common(lqmm::GemmFormat::Q4_K, 256, W, X, Y, M, N, K, stream);
+}
+
 size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
-  // The larger of the two formats' needs (a Q4_0 and a Q4_K call of these
-  // sizes), for the most row blocks any device's plan can have.
-  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(batch) || batch > kSmallMaxBatch) return 0;
+  // The largest need of any GEMV format's call of these sizes (passes of at
+  // most four activation rows), for the most row blocks any device's plan
+  // can have.
+  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(batch)) return 0;
+  using lqmm::GemvFormat;
   size_t best = 0;
-  for (lqmm::GemvFormat f : {lqmm::GemvFormat::Q4_0, lqmm::GemvFormat::Q4_K}) {
-    if (K % (f == lqmm::GemvFormat::Q4_K ? 256 : 32) != 0) continue;
+  for (GemvFormat f : {GemvFormat::Q4_0, GemvFormat::Q4_K, GemvFormat::Q8_0, GemvFormat::Q6_K,
+                       GemvFormat::Q2_K, GemvFormat::I4G32}) {
+    const int blk = (f == GemvFormat::Q4_K || f == GemvFormat::Q6_K || f == GemvFormat::Q2_K) ? 256 : 32;
+    if (K % blk != 0) continue;
+    const int64_t B = small_only(f) && batch > kSmallMaxBatch ? kSmallMaxBatch : batch;
+    if (B > kSmallMaxBatch) continue;
     lqmm::SmallGemvPlan sp;
     size_t need = 0;
-    if (plan_small(f, N, K, (int)batch, 1 << 30, &sp, &need) && need > best) best = need;
+    if (plan_small(f, N, K, (int)B, 1 << 30, &sp, &need) && need > best) best = need;
   }
   return best;
 }

@@ -1281,9 +1281,16 @@ size_t gemv_coal_stage_bytes(int u) {
 }
 
 int gemv_unit_weights(GemvFormat f) {
-  return f == GemvFormat::Q4_0 ? FmtQ4_0::kUnitWeights
-         : f == GemvFormat::Q4_0x2 ? FmtQ4_0x2::kUnitWeights
-                                   : FmtQ4_K::kUnitWeights;
+  switch (f) {
+    case GemvFormat::Q4_0: return FmtQ4_0::kUnitWeights;
+    case GemvFormat::Q4_0x2: return FmtQ4_0x2::kUnitWeights;
+    case GemvFormat::Q4_K: return FmtQ4_K::kUnitWeights;
+    case GemvFormat::Q8_0: return 32;   // FmtQ8_0: one block
+    case GemvFormat::Q6_K: return 128;  // FmtQ6_K: half a super-block
+    case GemvFormat::Q2_K: return 128;  // FmtQ2_K: half a super-block
+    case GemvFormat::I4G32: return 32;  // FmtI4G32: one group
+  }
+  return 32;
 }
 
 int gemv_threads() { return kGemvThreads; }

@@ -510,6 +510,29 @@ __device__ __forceinline__ XWord load_xword(const float *__restrict__ x, int64_t
   return XWord{*reinterpret_cast<const float4_t *>(base + F::x_lo(t)),
                *reinterpret_cast<const float4_t *>(base + F::x_hi(t))};
 }
+// Formats may declare kAcrossPairs = true: their weight words unpack to the
+// pairs (w0,w4), (w1,w5), (w2,w6), (w3,w7) of eight consecutive weights, and
+// the activations are paired the same way (see pack_xword_for). Formats may
+// also declare kAux = true: their units carry per-group values from
+// separate arrays (GemvAux), loaded by F::load_aux.
+template <class F, class = void>
+struct across_pairs : std::false_type {};
+template <class F>
+struct across_pairs<F, std::void_t<decltype(F::kAcrossPairs)>>
+    : std::integral_constant<bool, F::kAcrossPairs> {};
+template <class F, class = void>
+struct has_aux : std::false_type {};
+template <class F>
+struct has_aux<F, std::void_t<decltype(F::kAux)>> : std::integral_constant<bool, F::kAux> {};
+
+// Separate per-group arrays of a weight format (the int4 layout's fp32
+// scales and zero points): group g of row n at a[n * groups_per_row + g].
+struct GemvAux {
+  const float *a;
+  const float *b;
+  int64_t groups_per_row;
+};
+
 __device__ __forceinline__ u32x4 pack_xword(const XWord &w) {
   const float4_t hi = w.hi;
   u32x4 word;
@@ -518,6 +541,36 @@ __device__ __forceinline__ u32x4 pack_xword(const XWord &w) {
   word.z = pack_half2(w.lo.y, w.lo.w);
   word.w = pack_half2(hi.y, hi.w);
   return word;
+}
+
+// The activation word of a format: pack_xword's pairing, or for formats with
+// kAcrossPairs (lo = x0..x3, hi = x4..x7) the pairs (x0,x4), (x1,x5),
+// (x2,x6), (x3,x7). Either way word_sums' "lo" halves (x and z) go with the
+// words' low-nibble weights and its "hi" halves (y and w) with the high ones.
+template <class F>
+__device__ __forceinline__ u32x4 pack_xword_for(const XWord &w) {
+  if constexpr (across_pairs<F>::value) {
+    u32x4 word;
+    word.x = pack_half2(w.lo.x, w.hi.x);
+    word.y = pack_half2(w.lo.y, w.hi.y);
+    word.z = pack_half2(w.lo.z, w.hi.z);
+    word.w = pack_half2(w.lo.w, w.hi.w);
+    return word;
+  } else {
+    return pack_xword(w);
+  }
+}
+
+// Load unit `unit` of a row slice: the format's own load, or for formats with
+// separate per-group arrays its load_aux (row index and the slice's first
+// unit locate the groups).
+template <class F>
+__device__ __forceinline__ typename F::Raw load_unit(const uint8_t *rowp, uint32_t unit, int64_t row,
+                                                     int u0, const GemvAux &aux) {
+  if constexpr (has_aux<F>::value)
+    return F::load_aux(rowp, unit, row, u0, aux);
+  else
+    return F::load(rowp, unit);
 }
 
 // Staged words are grouped by word index t: word t of every (row, unit) pair
@@ -555,7 +608,7 @@ __device__ __forceinline__ void stage_words(u32x4 *xs, int nb, int nu, const flo
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (dst[k] >= 0) xs[dst[k]] = pack_xword(w[k]);
+      if (dst[k] >= 0) xs[dst[k]] = pack_xword_for<F>(w[k]);
   }
 }
 

@@ -38,7 +38,9 @@ hipError_t ensure_max_lds(int bytes) {
 // ---- GEMV -------------------------------------------------------------------
 // Q4_0x2: Q4_0 weights taken two blocks (64 weights, 36 bytes) per unit, used
 // by the VALU-mode kernel when K % 64 == 0.
-enum class GemvFormat { Q4_0, Q4_K, Q4_0x2 };
+// Q8_0, Q6_K, Q2_K and I4G32 (the int4 group-32 layout) run on the
+// small-problem kernel only.
+enum class GemvFormat { Q4_0, Q4_K, Q4_0x2, Q8_0, Q6_K, Q2_K, I4G32 };
 
 // Largest dynamic LDS one GEMV launch may use (staged activations + sums).
 constexpr int kMaxGemvLds = 144 * 1024;
@@ -102,8 +104,15 @@ struct SmallGemvPlan {
   int row_blocks;
   size_t lds_bytes;
   int64_t row_bytes, ldx, ldy, N;
+  // per-group arrays of formats that keep them apart (I4G32: scales, zeros)
+  const float *aux_a = nullptr, *aux_b = nullptr;
+  int64_t aux_groups = 0;  // groups per row
 };
 size_t gemv_small_lds_bytes(GemvFormat f, int batch, int nus);
+// the further formats' instances (gemv_small_more.hip)
+size_t gemv_small_lds_bytes_more(GemvFormat f, int batch, int nus);
+hipError_t gemv_small_launch_more(const SmallGemvPlan &plan, const uint8_t *W, const float *x,
+                                  float *y, float *partials, int *counters, hipStream_t stream);
 size_t gemv_small_max_lds();  // the most dynamic LDS a small-kernel plan may use
 hipError_t gemv_small_launch(const SmallGemvPlan &plan, const uint8_t *W, const float *x, float *y,
                              float *partials, int *counters, hipStream_t stream);
@@ -113,6 +122,11 @@ hipError_t gemv_small_clear_counters(int *counters, int n, hipStream_t stream);
 // ---- Q8_0 x fp16 GEMM ---------------------------------------------------------
 hipError_t gemm_q8_0_launch(const uint8_t *W, const uint16_t *X, uint16_t *Y, int64_t M,
                             int64_t N, int64_t K, int num_cus, hipStream_t stream);
+
+// ---- quantized x fp16 GEMM with dequantized fp16 weight tiles in LDS ----------
+enum class GemmFormat { Q8_0, Q4_0, Q4_K };
+hipError_t gemm_lds_launch(GemmFormat f, const uint8_t *W, const uint16_t *X, uint16_t *Y,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // ---- fp32 GEMM ----------------------------------------------------------------
 hipError_t sgemm_launch(const float *A, const float *B, float *C, int64_t M, int64_t N,

@@ -167,8 +167,69 @@ lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y,
                            int64_t N, int64_t K, int64_t batch,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The other format x phase pairs and more block formats. "Llamas na Web",
+ * "Design de Shader Consciente de Quantizacao" applies both kernel styles to
+ * every quantization format (mat-vec: dequantize in registers; matmul:
+ * dequantize into shared memory and reuse) and adds a format by adding its
+ * dequantization routine.
+ *
+ * Decode GEMVs y[b][n] = sum_k W[n][k] * x[b][k]; arguments, layouts,
+ * workspace and precision as for lqmm_gemv_q4_0 (x rounded to fp16, block
+ * scales applied in fp32, fp32 accumulation; every activation row on the
+ * vector ALUs, in passes of up to four rows). Split-K plans, for rows longer
+ * than one wave's slice (2048 weights of Q8_0 or the int4 layout, 4096 when
+ * N is at least four times the CU count; 8192 of Q6_K or Q2_K), need the
+ * workspace (LQMM_ERR_WORKSPACE without it).
+ *   lqmm_gemv_q8_0: W is N x (K/32) Q8_0 blocks (34 bytes), K % 32 == 0.
+ *   lqmm_gemv_q6_k: W is N x (K/256) Q6_K super-blocks (210 bytes), K % 256 ==
+ *     0. Super-block: [ql 128][qh 64][scales 16 x int8][d fp16];
+ *     w = d * scales[k/16] * (q - 32), q = 6 bits: weight k = 128h + 32j + l
+ *     (h < 2, j < 4, l < 32) has low 4 bits from the low (j < 2) or high
+ *     (j >= 2) nibble of ql[64h + 32(j%2) + l], high 2 bits from bits
+ *     2j..2j+1 of qh[32h + l].
+ *   lqmm_gemv_q2_k: W is N x (K/256) Q2_K super-blocks (84 bytes), K % 256 ==
+ *     0. Super-block: [scales 16][qs 64][d fp16][dmin fp16]; scales[g] =
+ *     sc | m << 4 for weights 16g..16g+15; w = d * sc * q - dmin * m, q =
+ *     bits 2j..2j+1 of qs[32h + l] for weight k = 128h + 32j + l.
+ *   lqmm_gemv_i4g32: the int4 layout of "Compute Shaders con WebGPU para
+ *     Inferencia ML", "Yendo a Cuantizado: Matmul INT4" (GPTQ/AWQ style):
+ *     Wq holds N*K/8 32-bit words, weight (n, k) being nibble (n*K + k) % 8
+ *     (bits 4i..4i+3) of word (n*K + k) / 8, a two's-complement code s in
+ *     -8..7; scales and zeros are fp32 arrays of N x K/32 (per row and group
+ *     of 32 along K); w = (s - zero) * scale. K % 32 == 0. (The page writes
+ *     result[row * N + col] with row = weight row; y here is batch x N like
+ *     every GEMV of this library.)
+ */
+lqmm_status lqmm_gemv_q8_0(const void *W, const float *x, float *y,
+                           int64_t N, int64_t K, int64_t batch,
+                           void *workspace, size_t workspace_bytes, void *stream);
+lqmm_status lqmm_gemv_q6_k(const void *W, const float *x, float *y,
+                           int64_t N, int64_t K, int64_t batch,
+                           void *workspace, size_t workspace_bytes, void *stream);
+lqmm_status lqmm_gemv_q2_k(const void *W, const float *x, float *y,
+                           int64_t N, int64_t K, int64_t batch,
+                           void *workspace, size_t workspace_bytes, void *stream);
+lqmm_status lqmm_gemv_i4g32(const uint32_t *Wq, const float *scales,
+                            const float *zeros, const float *x, float *y,
+                            int64_t N, int64_t K, int64_t batch,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Prefill GEMMs Y = X * W^T over Q4_0 (K % 32 == 0) and Q4_K (K % 256 == 0)
+ * weights: X is M x K fp16, Y is M x N fp16, fp32 accumulation, K <
+ * LQMM_GEMM_MAX_K. Each step's blocks are dequantized to fp16 into LDS
+ * tiles reused by the whole M tile: each weight rounded once to fp16 (Q4_0
+ * d*(q-8); Q4_K d*sc*q - dmin*m formed in fp32). Output rounded to nearest
+ * even.
+ */
+lqmm_status lqmm_gemm_q4_0_f16(const void *W, const uint16_t *X, uint16_t *Y,
+                               int64_t M, int64_t N, int64_t K, void *stream);
+lqmm_status lqmm_gemm_q4_k_f16(const void *W, const uint16_t *X, uint16_t *Y,
+                               int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Workspace the GEMV calls of these sizes can use, in bytes (0 = none):
- * enough for lqmm_gemv_q4_0 and lqmm_gemv_q4_k on any device. */
+ * enough for every GEMV entry point on any device. */
 size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch);
 
 /* Static, human-readable name of a status code. */

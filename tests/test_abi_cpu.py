@@ -70,24 +70,30 @@ def test_status_strings(lib):
 
 
 def test_workspace_query(lib, monkeypatch):
-    """The split-K workspace the planner asks for: none when one wave covers
-    a row slice; for longer rows one arrival counter per row block (256-byte
-    aligned) and S * batch * N fp32 partial sums."""
+    """The split-K workspace the planner may ask for, the largest over the
+    GEMV formats and over devices (one wave per workgroup, one unit per lane
+    at most): none when one wave covers a row slice of 64 units; otherwise
+    one arrival counter per row block (256-byte aligned) and S * batch * N
+    fp32 partial sums."""
     monkeypatch.delenv("LQMM_TUNE_GEMV_SPLITK", raising=False)
-    assert bq.lqmm_gemv_workspace_bytes(4096, 4096, 1) == 0
+    def need(rows_per_wave, N, S, B):
+        blocks = (N + rows_per_wave - 1) // rows_per_wave
+        return (blocks * 4 + 255) // 256 * 256 + S * B * N * 4
+    # K = 1024: every format's row fits one wave slice (Q8_0: 32 units)
     assert bq.lqmm_gemv_workspace_bytes(1024, 1024, 1) == 0
-    # K = 8192: 128 units of 64 weights, two slices of 64; one row per wave
-    # and one wave per workgroup at most: 100 counters
-    assert bq.lqmm_gemv_workspace_bytes(100, 8192, 2) == 512 + 2 * 2 * 100 * 4
-    # K = 16384 Q4_K: four slices
-    assert bq.lqmm_gemv_workspace_bytes(64, 16384, 1) == 256 + 4 * 1 * 64 * 4
-    # not a small problem, or more than four activation rows: none
-    assert bq.lqmm_gemv_workspace_bytes(28672, 8192, 1) == 0
-    assert bq.lqmm_gemv_workspace_bytes(100, 8192, 5) == 0
-    # a forced split at a configuration shape: 1024 x 1024 in two slices of
-    # 8 units (8 lanes per row, 8 rows per wave: 128 counters)
+    # K = 4096: Q8_0 and the int4 layout (32-weight units, 128 per row) split
+    # in two slices of 64 units, one row per wave
+    assert bq.lqmm_gemv_workspace_bytes(4096, 4096, 1) == need(1, 4096, 2, 1)
+    # K = 8192: 256 units of 32 weights, four slices
+    assert bq.lqmm_gemv_workspace_bytes(100, 8192, 2) == need(1, 100, 4, 2)
+    # K = 16384: eight slices
+    assert bq.lqmm_gemv_workspace_bytes(64, 16384, 1) == need(1, 64, 8, 1)
+    # more than four activation rows: passes of four
+    assert bq.lqmm_gemv_workspace_bytes(100, 8192, 5) == need(1, 100, 4, 4)
+    # a forced split at the 1024 x 1024 configuration: two slices of 16
+    # 32-weight units (16 lanes per row, 4 rows per wave)
     monkeypatch.setenv("LQMM_TUNE_GEMV_SPLITK", "2")
-    assert bq.lqmm_gemv_workspace_bytes(1024, 1024, 1) == 512 + 2 * 1 * 1024 * 4
+    assert bq.lqmm_gemv_workspace_bytes(1024, 1024, 1) == need(4, 1024, 2, 1)
 
 
 def test_workspace_alignment_checked(lib):
