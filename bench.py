@@ -120,8 +120,10 @@ class Rot:
 
 
 class Case:
-    def __init__(self, name, kind, bytes_, flops, launch, nrot, make_out, launch_warm=None):
+    def __init__(self, name, kind, bytes_, flops, launch, nrot, make_out, launch_warm=None,
+                 section="step"):
         self.name, self.kind = name, kind
+        self.section = section  # "step": the hot path; "next": further format x phase pairs
         self.bytes, self.flops = bytes_, flops
         self.launch = launch          # launch(): one call on the next weight copy
         self.launch_warm = launch_warm  # one call on the same weight copy every time
@@ -260,6 +262,64 @@ def build_cases(torch, only):
         cases.append(Case(name, "gemm_f32", alg, 2 * s.M * s.N * s.K, launch, R,
                           lambda C=C: C.cpu().numpy()))
         inputs[name] = ("sgemm", s.A, s.B, s.N, s.K)
+
+    # The other format x phase pairs and the further formats, at the same
+    # layer shapes (reported apart from the step: "next_formats").
+    next_gemv = {"q8_0": (bq.lqmm_gemv_q8_0, ["q8_0_gemv_4096x4096_b1", "q8_0_gemv_11008x4096_b1",
+                                              "q8_0_gemv_12288x4096_b4"]),
+                 "q6_k": (bq.lqmm_gemv_q6_k, ["q6_k_gemv_11008x4096_b1"]),
+                 "q2_k": (bq.lqmm_gemv_q2_k, ["q2_k_gemv_11008x4096_b1"])}
+    for fmt, (fn, names) in next_gemv.items():
+        for name in names:
+            if not want(name):
+                continue
+            c = synth.make(name)
+            wbytes = c.W.nbytes
+            R = rot(wbytes)
+            Ws = rotset(c.W, R)
+            x = torch.from_numpy(c.x.copy()).to(dev)
+            y = torch.empty((c.batch, c.N), dtype=torch.float32, device=dev)
+
+            def launch(Ws=Ws, x=x, y=y, N=c.N, fn=fn):
+                fn(Ws.next(), x, N, out=y)
+
+            cases.append(Case(name, "gemv", wbytes + c.batch * c.K * 4 + c.batch * c.N * 4,
+                              2 * c.batch * c.N * c.K, launch, R, lambda y=y: y.cpu().numpy(),
+                              section="next"))
+    name = "i4g32_gemv_11008x4096_b1"
+    if want(name):
+        c = synth.make(name)
+        wbytes = c.Wq.nbytes + c.scales.nbytes + c.zeros.nbytes
+        R = rot(wbytes)
+        Wq, sc, z = copies(c.Wq.view(np.int32), R), copies(c.scales, R), copies(c.zeros, R)
+        trio = Rot([(Wq[i], sc[i].view(c.N, -1), z[i].view(c.N, -1)) for i in range(R)])
+        x = torch.from_numpy(c.x.copy()).to(dev)
+        y = torch.empty((c.batch, c.N), dtype=torch.float32, device=dev)
+
+        def launch(trio=trio, x=x, y=y, N=c.N):
+            a, b, d = trio.next()
+            bq.lqmm_gemv_i4g32(a, b, d, x, N, out=y)
+
+        cases.append(Case(name, "gemv", wbytes + c.batch * c.K * 4 + c.batch * c.N * 4,
+                          2 * c.batch * c.N * c.K, launch, R, lambda y=y: y.cpu().numpy(),
+                          section="next"))
+    for fmt, fn in (("q4_0", bq.lqmm_gemm_q4_0_f16), ("q4_k", bq.lqmm_gemm_q4_k_f16)):
+        name = f"{fmt}_gemm_512x14336x4096"
+        if not want(name):
+            continue
+        cg = synth.make(name)
+        wbytes = cg.W.nbytes
+        R = rot(wbytes)
+        Ws = rotset(cg.W, R)
+        X = torch.from_numpy(cg.X).to(dev)
+        Y = torch.empty((cg.M, cg.N), dtype=torch.float16, device=dev)
+
+        def launch(Ws=Ws, X=X, Y=Y, N=cg.N, fn=fn):
+            fn(Ws.next(), X, N, out=Y)
+
+        cases.append(Case(name, "gemm_f16", wbytes + cg.M * cg.K * 2 + cg.M * cg.N * 2,
+                          2 * cg.M * cg.N * cg.K, launch, R, lambda Y=Y: Y.cpu().numpy(),
+                          section="next"))
     return cases, inputs, stream_sets
 
 
@@ -704,8 +764,10 @@ def main():
     # events on the launch stream. This is the same work as K step-major
     # passes, with the graph-launch overhead spread over K launches; the
     # events give each call's average launch duration inside the timed region.
-    gemv = [c for c in cases if c.kind == "gemv"]
-    order = gemv + [c for c in cases if c.kind != "gemv"]
+    step = [c for c in cases if c.section == "step"]
+    gemv = [c for c in step if c.kind == "gemv"]
+    order = gemv + [c for c in step if c.kind != "gemv"]
+    extra = [c for c in cases if c.section == "next"]
     # One eager call of each case before any capture: the binding's split-K
     # workspaces and the library's once-per-device set-up happen outside the
     # graphs.
@@ -759,6 +821,32 @@ def main():
         marker(1)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
+    # The further format x phase pairs, after the timed steps and timed the
+    # same way (a settle of up to 50 ms of replays, then a graph of --steps
+    # launches per case between HIP events).
+    if extra:
+        xrun = {}
+        for c in extra:
+            c.launch()
+        torch.cuda.synchronize()
+        for c in extra:
+            xrun[c.name] = capture(torch, lambda c=c: [c.launch() for _ in range(args.steps)])
+            xw = capture(torch, lambda c=c: [c.launch() for _ in range(max(args.warmup, 5))])
+            t_settle = time.perf_counter()
+            while True:
+                xw.replay()
+                torch.cuda.synchronize()
+                if (time.perf_counter() - t_settle) * 1e3 >= min(args.settle_ms, 50.0):
+                    break
+        xev = [torch.cuda.Event(enable_timing=True) for _ in range(len(extra) + 1)]
+        xev[0].record()
+        for i, c in enumerate(extra):
+            xrun[c.name].replay()
+            xev[i + 1].record()
+        torch.cuda.synchronize()
+        for i, c in enumerate(extra):
+            c.avg_ms = xev[i].elapsed_time(xev[i + 1]) / args.steps
+            print(f"[bench] {c.name}: {case_summary(c)}", file=sys.stderr, flush=True)
     for i, c in enumerate(order):
         c.avg_ms = ev[i].elapsed_time(ev[i + 1]) / args.steps
         print(f"[bench] {c.name}: {case_summary(c)}", file=sys.stderr, flush=True)
@@ -808,6 +896,9 @@ def main():
             line[key] = {"tflops": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4),
                          "ms": round(gc.avg_ms, 6)}
     line["cases"] = {c.name: case_summary(c) for c in order}
+    if extra:
+        line["next_formats"] = {c.name: dict(case_summary(c), roofline=roofline_entry(c))
+                                for c in extra}
     if not args.no_context:
         try:
             line["context"] = measure_context(torch, cases, stream_sets, args.steps)
