@@ -639,3 +639,32 @@ def test_concurrent_first_calls(tmp_path):
                        timeout=110)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     assert "threads ok" in r.stdout
+
+
+def test_decode_chain_graph_replays(orc):
+    """The decode-layer GEMV chain captured in one HIP graph: every replay
+    (with eager work and synchronizations between replays) reproduces the
+    eager pass bit for bit, and the chain's first GEMV matches the oracle."""
+    import torch
+    from block_quantized_matmul_amd.chain import LAYER, DecodeChain
+    announce("decode chain graph replays")
+    ch = DecodeChain(torch, layers=1, seed=3)
+    ch.run()
+    torch.cuda.synchronize()
+    eager = [host(o).copy() for o in ch.outs]
+    g = ch.capture()
+    scratch = torch.randn(1 << 16, device="cuda:0")
+    for i in range(3):
+        for o in ch.outs:
+            o.fill_(float("nan"))
+        scratch.mul_(1.0001)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(ch.outs, eager):
+            assert np.array_equal(host(o), e), i
+    assert np.isfinite(eager[-1]).all()
+    N, K = LAYER[0][1], LAYER[0][2]
+    W0 = host(ch.layers[0][0]).reshape(N, -1)
+    ref = orc.gemv_q4_0(W0, host(ch.x), N, K)
+    assert_close(eager[0], ref, TOL_QUANT, "chain qkv")
