@@ -85,7 +85,7 @@ def load():
     lib.lqmm_gemm_q8_0_f16.restype = st
     lib.lqmm_gemv_workspace_bytes.argtypes = [i64, i64, i64]
     lib.lqmm_gemv_workspace_bytes.restype = sz
-    lib.lqmm_status_string.argtypes = [st]
+    lib.lqmm_status_string.argtypes = [ctypes.c_int]
     lib.lqmm_status_string.restype = ctypes.c_char_p
     lib.lqmm_version.argtypes = []
     lib.lqmm_version.restype = ctypes.c_int

@@ -622,13 +622,13 @@ size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
   return best;
 }
 
-const char *lqmm_status_string(lqmm_status s) {
+const char *lqmm_status_string(int s) {
   switch (s) {
     case LQMM_OK: return "LQMM_OK";
     case LQMM_ERR_NULL: return "LQMM_ERR_NULL: a required pointer is NULL";
     case LQMM_ERR_SHAPE: return "LQMM_ERR_SHAPE: a size is out of range or not a block multiple";
     case LQMM_ERR_ALIGN: return "LQMM_ERR_ALIGN: a pointer is not 16-byte aligned";
-    case LQMM_ERR_WORKSPACE: return "LQMM_ERR_WORKSPACE: workspace argument inconsistent";
+    case LQMM_ERR_WORKSPACE: return "LQMM_ERR_WORKSPACE: the call needs a larger workspace";
     case LQMM_ERR_DEVICE: return "LQMM_ERR_DEVICE: no usable gfx950 device";
     case LQMM_ERR_LAUNCH: return "LQMM_ERR_LAUNCH: kernel launch failed";
   }

@@ -191,8 +191,11 @@ def main():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--json", default="")
     p.add_argument("--md", default="")
+    p.add_argument("--family", default="", choices=["", "small", "valu", "mfma"],
+                   help="sweep one family of overrides only")
     args = p.parse_args()
-    rep = sweep(args.case, args.steps)
+    fam = {"small": GEMV_SMALL, "valu": GEMV_VALU, "mfma": GEMV_MFMA}
+    rep = sweep(args.case, args.steps, fam.get(args.family))
     if args.json:
         with open(args.json, "w") as f:
             json.dump(rep, f, indent=1)

@@ -84,7 +84,7 @@ typedef enum {
   LQMM_ERR_NULL = 1,      /* a required pointer is NULL */
   LQMM_ERR_SHAPE = 2,     /* a size is <= 0, not a block multiple, or too large */
   LQMM_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
-  LQMM_ERR_WORKSPACE = 4, /* reserved: workspace argument inconsistent */
+  LQMM_ERR_WORKSPACE = 4, /* the call needs a workspace (split-K partial sums) and got none or too small a one */
   LQMM_ERR_DEVICE = 5,    /* no usable HIP device, or it is not a gfx950 GPU */
   LQMM_ERR_LAUNCH = 6     /* a kernel launch failed (hipGetLastError) */
 } lqmm_status;
@@ -232,8 +232,10 @@ lqmm_status lqmm_gemm_q4_k_f16(const void *W, const uint16_t *X, uint16_t *Y,
  * enough for every GEMV entry point on any device. */
 size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch);
 
-/* Static, human-readable name of a status code. */
-const char *lqmm_status_string(lqmm_status s);
+/* Static, human-readable name of a status code. Takes any int (a status
+ * code read back from elsewhere may hold any value); values that are not an
+ * lqmm_status give a static "unknown status" string. */
+const char *lqmm_status_string(int s);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int lqmm_version(void);
