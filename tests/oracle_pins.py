@@ -140,7 +140,7 @@ def pin_gemm_q4_worked(o):
 def pin_q6_k_worked(o):
     g = read_golden("q6_k_block.txt")
     K = 256
-    for blk in ("a", "b"):
+    for blk in ("a", "b", "c"):
         W = _hex(g[f"{blk}_hex"])
         assert W.size == 210
         for key, v in g.items():
