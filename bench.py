@@ -100,6 +100,9 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=3, metavar=("PMC_DIR", "CALIB_MIB", "COMMAND"),
                    help="host only: write the GEMV cases' HBM traffic summary from rocprofv3 "
                         "--pmc runs under PMC_DIR/<case>.fetch and PMC_DIR/<case>.write")
+    p.add_argument("--summarize-counters", nargs=3, metavar=("PMC_DIR", "OUT_MD", "COMMAND"),
+                   help="host only: write a markdown summary of rocprofv3 --kernel-trace --pmc "
+                        "passes over the GEMM cases (PMC_DIR/pass<n>/)")
     p.add_argument("--eager", action="store_true",
                    help="launch from Python one call at a time instead of replaying HIP graphs")
     return p.parse_args()
@@ -323,15 +326,41 @@ def build_cases(torch, only):
     return cases, inputs, stream_sets
 
 
+_capture_stream = None
+
+
+def capture_stream(torch):
+    """The one stream every graph is captured on. The binding keys its
+    default split-K workspaces by stream: calls made eagerly on this stream
+    before capture allocate them, so that no allocation (and no zero fill)
+    is recorded into a graph."""
+    global _capture_stream
+    if _capture_stream is None:
+        _capture_stream = torch.cuda.Stream()
+    return _capture_stream
+
+
 def capture(torch, fn):
     """A HIP graph of fn()'s launches (the library launches on the current
     stream, which is the capture stream inside the context). Replaying it
-    removes the Python call overhead between kernels; it records only kernel
-    nodes (no memset nodes)."""
+    removes the Python call overhead between kernels; it records only the
+    library's kernel nodes (no memset or fill nodes: run fn() once eagerly
+    on capture_stream() first)."""
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=capture_stream(torch)):
         fn()
     return g
+
+
+def eager_on_capture_stream(torch, cases):
+    """One eager call of each case on the capture stream (workspaces and the
+    library's once-per-device set-up happen outside the graphs)."""
+    s = capture_stream(torch)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in cases:
+            c.launch()
+    torch.cuda.synchronize()
 
 
 def case_summary(c):
@@ -442,8 +471,13 @@ def measure_context(torch, cases, stream_sets, steps):
     ctx = {}
 
     def graph_ms(fn, n):
-        for _ in range(3):  # outside the capture: library set-up (hipBLASLt's) and warm-up
-            fn()
+        # outside the capture, on the capture stream: library set-up
+        # (hipBLASLt's, the binding's workspaces) and warm-up
+        s = capture_stream(torch)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                fn()
         torch.cuda.synchronize()
         g = capture(torch, lambda: [fn() for _ in range(n)])
         g.replay()
@@ -757,8 +791,86 @@ def summarize_traffic(pmc_dir, calib_mib, command):
     print(json.dumps(out, indent=1))
 
 
+def summarize_counters(pmc_dir, out_md, command):
+    """Markdown summary of rocprofv3 `--kernel-trace --pmc` passes over the
+    GEMM cases (PMC_DIR/pass<n>/...): per library kernel, the mean per
+    dispatch of every counter collected, the mean kernel duration from the
+    same pass's trace, and ratios stated with their formulas. Counter values
+    are summed over the GPU's instances by rocprofv3."""
+    import csv
+    import glob
+    per_kernel = {}  # kernel -> {counter: [values per dispatch]}
+    durs = {}        # kernel -> [us]
+    for pdir in sorted(glob.glob(os.path.join(pmc_dir, "pass*"))):
+        vals = {}
+        for r in csv.DictReader(open(_find(pdir, "counter_collection.csv"))):
+            if "lqmm::" not in r["Kernel_Name"]:
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            k = _short_kernel(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(key, 0.0)
+            vals[k][key] += float(r["Counter_Value"])
+        for k, d in vals.items():
+            for (_, cn), v in d.items():
+                per_kernel.setdefault(k, {}).setdefault(cn, []).append(v)
+        for r in csv.DictReader(open(_find(pdir, "kernel_trace.csv"))):
+            if "lqmm::" in r["Kernel_Name"]:
+                k = _short_kernel(r["Kernel_Name"])
+                durs.setdefault(k, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    mean = lambda v: sum(v) / len(v)
+    out = ["# Matrix-core and LDS counters of the GEMM kernels\n\n",
+           "Commands, from the repository root on one MI355X after "
+           "`cd /tmp && export TMPDIR=/tmp` (one rocprofv3 pass per counter group, "
+           "paths relative to the repository):\n\n", f"```\n{command}\n```\n\n",
+           "Means per dispatch over every launch of the kernel in the passes (warmup and "
+           "timed launches of the cases, cold weights). Durations are from the kernel trace "
+           "taken in the same passes.\n\n"]
+    for k in sorted(per_kernel):
+        c = {cn: mean(v) for cn, v in per_kernel[k].items()}
+        n = max(len(v) for v in per_kernel[k].values())
+        d = mean(durs.get(k, [float("nan")]))
+        out.append(f"## `{k}`\n\n{n} dispatches per counter; mean duration {d:.2f} us.\n\n"
+                   "| counter | mean per dispatch |\n|---|---:|\n")
+        for cn in sorted(c):
+            out.append(f"| {cn} | {c[cn]:,.0f} |\n")
+        out.append("\n")
+        ratios = []
+        g = c.get("GRBM_GUI_ACTIVE")
+        if g:
+            ratios.append(("GRBM_GUI_ACTIVE / duration (GHz x counted instances)",
+                           g / (d * 1e3)))
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            ratios.append(("SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs)",
+                           c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 256)))
+        if "SQ_BUSY_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            ratios.append(("SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES",
+                           c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_BUSY_CYCLES"]))
+        for mops, peak in (("SQ_INSTS_VALU_MFMA_MOPS_F16", F16_PEAK_TFLOPS),
+                           ("SQ_INSTS_VALU_MFMA_MOPS_F32", F32_PEAK_TFLOPS)):
+            if c.get(mops):
+                ratios.append((f"{mops} x 512 / duration (TFLOP/s issued to the matrix cores)",
+                               c[mops] * 512 / (d * 1e-6) / 1e12))
+                ratios.append((f"  the same against the peak ({peak:g} TFLOP/s)",
+                               c[mops] * 512 / (d * 1e-6) / 1e12 / peak))
+        if c.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in c:
+            ratios.append(("SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+                           c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
+        if ratios:
+            out.append("| ratio | value |\n|---|---:|\n")
+            for name, v in ratios:
+                out.append(f"| {name} | {v:.4g} |\n")
+            out.append("\n")
+    with open(out_md, "w") as f:
+        f.write("".join(out))
+    print("".join(out))
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
         return
@@ -810,12 +922,12 @@ def main():
     gemv = [c for c in step if c.kind == "gemv"]
     order = gemv + [c for c in step if c.kind != "gemv"]
     extra = [c for c in cases if c.section == "next"]
-    # One eager call of each case before any capture: the binding's split-K
-    # workspaces and the library's once-per-device set-up happen outside the
-    # graphs.
+    # One eager call of each case before any capture, on the capture stream:
+    # the binding's split-K workspaces and the library's once-per-device
+    # set-up happen outside the graphs.
     for c in order:
         c.launch()
-    torch.cuda.synchronize()
+    eager_on_capture_stream(torch, order)
     if args.eager:
         run = {c.name: (lambda c=c, n=args.steps: [c.launch() for _ in range(n)]) for c in order}
         warm = {c.name: (lambda c=c, n=args.warmup: [c.launch() for _ in range(n)]) for c in order}
@@ -875,7 +987,7 @@ def main():
         xrun = {}
         for c in extra:
             c.launch()
-        torch.cuda.synchronize()
+        eager_on_capture_stream(torch, extra)
         for c in extra:
             xrun[c.name] = capture(torch, lambda c=c: [c.launch() for _ in range(args.steps)])
             xrun[c.name].replay()  # first replay (upload) untimed

@@ -104,11 +104,16 @@ def _setup(torch, name):
 
 
 def _time(torch, launch, steps, reps=3):
-    for _ in range(3):
-        launch()
+    # warm-up calls on the capture stream: the binding's per-stream workspace
+    # is allocated there, outside the graph (no zero fill recorded into it)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            launch()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         for _ in range(steps):
             launch()
     t0 = time.perf_counter()
