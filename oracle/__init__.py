@@ -51,11 +51,11 @@ class Oracle:
         lib.lqmm_oracle_f16_array_to_f64.argtypes = [_p, _p, _i64]
         for name in ("lqmm_oracle_dequant_q4_0", "lqmm_oracle_dequant_q8_0",
                      "lqmm_oracle_dequant_q4_k", "lqmm_oracle_dequant_q6_k",
-                     "lqmm_oracle_dequant_q2_k"):
+                     "lqmm_oracle_dequant_q2_k", "lqmm_oracle_dequant_q1_0"):
             getattr(lib, name).argtypes = [_p, _i64, _i64, _p]
         lib.lqmm_oracle_dequant_i4g32.argtypes = [_p, _p, _p, _i64, _i64, _p]
         for name in ("lqmm_oracle_gemv_q4_0", "lqmm_oracle_gemv_q4_k", "lqmm_oracle_gemv_q8_0",
-                     "lqmm_oracle_gemv_q6_k", "lqmm_oracle_gemv_q2_k"):
+                     "lqmm_oracle_gemv_q6_k", "lqmm_oracle_gemv_q2_k", "lqmm_oracle_gemv_q1_0"):
             getattr(lib, name).argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64]
         lib.lqmm_oracle_gemv_i4g32.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64]
         for name in ("lqmm_oracle_gemm_q8_0_f16", "lqmm_oracle_gemm_q4_0_f16",
@@ -109,6 +109,9 @@ class Oracle:
     def dequant_q2_k(self, W, N, K):
         return self._dequant("lqmm_oracle_dequant_q2_k", W, N, K)
 
+    def dequant_q1_0(self, W, N, K):
+        return self._dequant("lqmm_oracle_dequant_q1_0", W, N, K)
+
     def dequant_i4g32(self, Wq, scales, zeros, N, K):
         Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
         sc = np.ascontiguousarray(scales, dtype=np.float32)
@@ -153,6 +156,9 @@ class Oracle:
 
     def gemv_q2_k(self, W, x, N, K, rows=None) -> np.ndarray:
         return self._gemv("lqmm_oracle_gemv_q2_k", W, x, N, K, rows)
+
+    def gemv_q1_0(self, W, x, N, K, rows=None) -> np.ndarray:
+        return self._gemv("lqmm_oracle_gemv_q1_0", W, x, N, K, rows)
 
     def gemv_i4g32(self, Wq, scales, zeros, x, N, K, rows=None) -> np.ndarray:
         """The int4 group-32 layout: Wq uint32 words (N*K/8), scales and zeros

@@ -52,6 +52,11 @@
  *     one pair per 16 weights), qs[64], fp16 d at bytes 80-81, fp16 dmin at
  *     bytes 82-83; w = d * sc[k/16] * q - dmin * m[k/16], q in 0..3. Weight
  *     k = 128h + 32j + l takes bits 2j..2j+1 of qs[32h + l].
+ * q1_0, the 1-bit format "Resumo Tecnico: Llamas na Web" names under
+ * "Extensibilidade" without giving its bytes; read as the _0 family at one
+ * bit per weight: 6 bytes per 32 weights, bytes 0-1 fp16 d, bytes 2-5 the
+ * 32 code bits, weight j's bit c = bit (j % 8) of byte 2 + j / 8 (least
+ * significant bit first); w = d * (2c - 1), i.e. -d or +d.
  * A weight matrix of N output rows and K inputs stores row n as K/32 (or
  * K/256) consecutive blocks; rows are consecutive with no padding.
  *
@@ -229,6 +234,23 @@ static void deq_q2_k_block(const uint8_t *blk, double *w) {
   }
 }
 
+/* Dequantize one q1_0 block (6 bytes) into 32 doubles: w = d * (2c - 1). */
+static void deq_q1_0_block(const uint8_t *blk, double *w) {
+  double d = lqmm_oracle_f16_to_f64(rd16(blk));
+  for (int j = 0; j < QK; ++j) {
+#if LQMM_ORACLE_MUTANT == 17
+    int c = (blk[2 + j / 8] >> (7 - j % 8)) & 1; /* most significant bit first */
+#else
+    int c = (blk[2 + j / 8] >> (j % 8)) & 1;
+#endif
+#if LQMM_ORACLE_MUTANT == 18
+    w[j] = d * c; /* codes read as 0 / +d instead of -d / +d */
+#else
+    w[j] = d * (2 * c - 1);
+#endif
+  }
+}
+
 /* ---- dense dequantization of whole rows (exposed for the pins) ---- */
 
 void lqmm_oracle_dequant_q4_0(const uint8_t *W, int64_t N, int64_t K, double *out) {
@@ -236,6 +258,13 @@ void lqmm_oracle_dequant_q4_0(const uint8_t *W, int64_t N, int64_t K, double *ou
   for (int64_t n = 0; n < N; ++n)
     for (int64_t b = 0; b < nb; ++b)
       deq_q4_0_block(W + (n * nb + b) * 18, out + n * K + b * QK);
+}
+
+void lqmm_oracle_dequant_q1_0(const uint8_t *W, int64_t N, int64_t K, double *out) {
+  int64_t nb = K / QK;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t b = 0; b < nb; ++b)
+      deq_q1_0_block(W + (n * nb + b) * 6, out + n * K + b * QK);
 }
 
 void lqmm_oracle_dequant_q8_0(const uint8_t *W, int64_t N, int64_t K, double *out) {
@@ -321,6 +350,10 @@ static void row_q6_k(const uint8_t *W, int64_t n, int64_t K, double *w) {
   int64_t nb = K / QKK;
   for (int64_t b = 0; b < nb; ++b) deq_q6_k_block(W + (n * nb + b) * 210, w + b * QKK);
 }
+static void row_q1_0(const uint8_t *W, int64_t n, int64_t K, double *w) {
+  int64_t nb = K / QK;
+  for (int64_t b = 0; b < nb; ++b) deq_q1_0_block(W + (n * nb + b) * 6, w + b * QK);
+}
 static void row_q2_k(const uint8_t *W, int64_t n, int64_t K, double *w) {
   int64_t nb = K / QKK;
   for (int64_t b = 0; b < nb; ++b) deq_q2_k_block(W + (n * nb + b) * 84, w + b * QKK);
@@ -384,6 +417,11 @@ void lqmm_oracle_gemv_q8_0(const uint8_t *W, const float *x, double *y, int64_t 
 void lqmm_oracle_gemv_q6_k(const uint8_t *W, const float *x, double *y, int64_t N,
                            int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
   gemv_generic(row_q6_k, W, x, y, N, K, batch, rows, nrows);
+}
+
+void lqmm_oracle_gemv_q1_0(const uint8_t *W, const float *x, double *y, int64_t N,
+                           int64_t K, int64_t batch, const int64_t *rows, int64_t nrows) {
+  gemv_generic(row_q1_0, W, x, y, N, K, batch, rows, nrows);
 }
 
 void lqmm_oracle_gemv_q2_k(const uint8_t *W, const float *x, double *y, int64_t N,

@@ -24,6 +24,8 @@ available; these seeded layers stand in for them):
   q ~ U{0..63}, x ~ N(0,1) fp32.
 * Q2_K decode GEMV: d, dmin = |N(0,1)| * 0.01, 4-bit sc, m ~ U{0..15}, 2-bit
   q ~ U{0..3}, x ~ N(0,1) fp32.
+* q1_0 decode GEMV (1-bit codes): d = |N(0,1)| * 0.02, codes c ~ U{0, 1}
+  (weights -d or +d), x ~ N(0,1) fp32.
 * int4 group-32 GEMV (GPTQ/AWQ-style layout): fp32 scales |N(0,1)| * 0.02,
   signed codes s ~ U{-8..7}, fp32 zero points ~ U{-8..7} (integers),
   x ~ N(0,1) fp32.
@@ -34,7 +36,8 @@ from float64 with IEEE round-to-nearest-even (``astype(np.float16)``).
 
 Byte layouts (llama.cpp / GGUF style; the pages name the formats, not their
 bytes): see ``pack_q4_0``, ``pack_q8_0``, ``pack_q4_k``, ``pack_q6_k`` and
-``pack_q2_k``; the int4 layout of the pages' int4 matmul: ``pack_i4g32``.
+``pack_q2_k``; the 1-bit q1_0 reading: ``pack_q1_0``; the int4 layout of the
+pages' int4 matmul: ``pack_i4g32``.
 """
 from __future__ import annotations
 
@@ -47,6 +50,7 @@ Q8_0_BYTES = 34   # per 32 weights
 Q4_K_BYTES = 144  # per 256 weights
 Q6_K_BYTES = 210  # per 256 weights
 Q2_K_BYTES = 84   # per 256 weights
+Q1_0_BYTES = 6    # per 32 weights
 
 
 def _f16_bytes(a: np.ndarray) -> np.ndarray:
@@ -164,6 +168,20 @@ def pack_q2_k(d, dmin, sc, m, q) -> np.ndarray:
     return np.ascontiguousarray(blk.reshape(N, nsb * Q2_K_BYTES))
 
 
+def pack_q1_0(d: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Pack q1_0 blocks: [d (2 bytes LE)][32 code bits in 4 bytes], the bit
+    of weight j at bit j % 8 of byte j // 8 (least significant bit first).
+
+    d: (N, K/32) float16 scales. c: (N, K) codes in {0, 1}.
+    Returns (N, K/32 * 6) uint8.
+    """
+    N, K = c.shape
+    nb = K // 32
+    bits = np.packbits(c.astype(np.uint8).reshape(N, nb, 32), axis=-1, bitorder="little")
+    blk = np.concatenate([_f16_bytes(d.reshape(N, nb)), bits], axis=-1)
+    return np.ascontiguousarray(blk.reshape(N, nb * Q1_0_BYTES))
+
+
 def pack_i4g32(s: np.ndarray) -> np.ndarray:
     """Pack signed 4-bit codes, eight per 32-bit word: code (n, k) is nibble
     (n*K + k) % 8 (bits 4i..4i+3) of word (n*K + k) // 8, two's complement.
@@ -220,6 +238,17 @@ class Q8_0GemvCase:
     x: np.ndarray      # (batch, K) float32
     d: np.ndarray
     q: np.ndarray      # (N, K) int8
+    N: int
+    K: int
+    batch: int
+
+
+@dataclasses.dataclass
+class Q1_0Case:
+    W: np.ndarray      # (N, K/32*6) uint8
+    x: np.ndarray      # (batch, K) float32
+    d: np.ndarray      # (N, K/32) float16
+    c: np.ndarray      # (N, K) uint8 codes in {0, 1}
     N: int
     K: int
     batch: int
@@ -360,6 +389,15 @@ def q2_k_case(N: int, K: int, batch: int = 1, seed: int = 0, scale: float = 0.01
     return Q2_KCase(pack_q2_k(d, dmin, sc, m, q), x, d, dmin, sc, m, q, N, K, batch)
 
 
+def q1_0_case(N: int, K: int, batch: int = 1, seed: int = 0, scale: float = 0.02) -> Q1_0Case:
+    assert K % 32 == 0
+    rng = np.random.default_rng(seed)
+    d = _half_normal_f16(rng, (N, K // 32), scale)
+    c = rng.integers(0, 2, size=(N, K), dtype=np.uint8)
+    x = rng.standard_normal((batch, K)).astype(np.float32)
+    return Q1_0Case(pack_q1_0(d, c), x, d, c, N, K, batch)
+
+
 def i4g32_case(N: int, K: int, batch: int = 1, seed: int = 0, scale: float = 0.02) -> I4G32Case:
     assert K % 32 == 0
     rng = np.random.default_rng(seed)
@@ -405,6 +443,7 @@ CONFIGS = {
     "q6_k_gemv_11008x4096_b1": dict(kind="q6_k", N=11008, K=4096, batch=1),
     "q2_k_gemv_11008x4096_b1": dict(kind="q2_k", N=11008, K=4096, batch=1),
     "i4g32_gemv_11008x4096_b1": dict(kind="i4g32", N=11008, K=4096, batch=1),
+    "q1_0_gemv_11008x4096_b1": dict(kind="q1_0", N=11008, K=4096, batch=1),
 }
 
 
@@ -427,6 +466,8 @@ def make(name: str, seed: int = 0):
         return q4_k_gemm_case(c["M"], c["N"], c["K"], seed)
     if kind == "q6_k":
         return q6_k_case(c["N"], c["K"], c["batch"], seed)
+    if kind == "q1_0":
+        return q1_0_case(c["N"], c["K"], c["batch"], seed)
     if kind == "q2_k":
         return q2_k_case(c["N"], c["K"], c["batch"], seed)
     if kind == "i4g32":

@@ -165,6 +165,20 @@ def pin_q2_k_worked(o):
             assert o.gemv_q2_k(W, x, 1, K)[0, 0] == float(v), (key, o.gemv_q2_k(W, x, 1, K))
 
 
+def pin_q1_0_worked(o):
+    g = read_golden("q1_0_block.txt")
+    K = 32
+    for blk in ("a", "b"):
+        W = _hex(g[f"{blk}_hex"])
+        assert W.size == 6
+        for key, v in g.items():
+            if not key.startswith(blk + "_") or key.endswith("hex"):
+                continue
+            what = key[2:]
+            x = np.ones((1, K), np.float32) if what == "ones" else _onehot(K, int(what[1:]))
+            assert o.gemv_q1_0(W, x, 1, K)[0, 0] == float(v), (key, o.gemv_q1_0(W, x, 1, K))
+
+
 def pin_i4g32_worked(o):
     g = read_golden("i4g32_block.txt")
     K = 64
@@ -214,6 +228,9 @@ def pin_packers_match_golden(o):
     b2 = synth.pack_q2_k(one, np.array([[0.0]], np.float16), np.ones((1, 1, 16)),
                          np.zeros((1, 1, 16)), qb.astype(np.uint8)[None])
     assert b2.tobytes().hex() == g2["b_hex"]
+    g1 = read_golden("q1_0_block.txt")
+    cb = np.unpackbits(np.array([0x01, 0x80, 0xF0, 0x0F], np.uint8), bitorder="little")[None]
+    assert synth.pack_q1_0(np.array([[0.5]], np.float16), cb).tobytes().hex() == g1["b_hex"]
     gi = read_golden("i4g32_block.txt")
     codes = np.concatenate([np.arange(8), np.arange(-8, 0)] * 4)[None]
     assert synth.pack_i4g32(codes).astype("<u4").tobytes().hex() == gi["words_hex"]
@@ -268,6 +285,12 @@ def pin_round_trip(o):
     q2rec = (w2[ok2] + m2[ok2] * mm2[ok2]) / (d2[ok2] * s2[ok2])
     assert np.array_equal(np.rint(q2rec), c2.q.astype(np.float64)[ok2])
     assert np.allclose(q2rec, c2.q.astype(np.float64)[ok2], rtol=0, atol=1e-9)
+
+    c1 = synth.q1_0_case(9, 256, seed=35)
+    w1 = o.dequant_q1_0(c1.W, c1.N, c1.K)
+    d1 = c1.d.astype(np.float64).repeat(32, axis=1)
+    nz = d1 != 0
+    assert np.array_equal((w1[nz] / d1[nz] + 1) / 2, c1.c.astype(np.float64)[nz])
 
     ci = synth.i4g32_case(7, 128, seed=33)
     wi = o.dequant_i4g32(ci.Wq, ci.scales, ci.zeros, ci.N, ci.K)
@@ -380,6 +403,12 @@ def pin_closed_forms_new_formats(o):
     ref = (c2.d[:, :1].astype(np.float64) * (c2.sc[:, 0] * qsum).sum(-1, keepdims=True)
            - 16 * c2.dmin[:, :1].astype(np.float64) * c2.m[:, 0].sum(-1, keepdims=True))[:, 0]
     assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+    c1 = synth.q1_0_case(6, 96, seed=47)
+    y = o.gemv_q1_0(c1.W, np.ones((1, 96), np.float32), c1.N, 96)[0]
+    pop = c1.c.reshape(c1.N, 3, 32).astype(np.int64).sum(-1)
+    assert np.array_equal(y, (c1.d.astype(np.float64) * (2 * pop - 32)).sum(-1))
+    col = o.gemv_q1_0(c1.W, _onehot(96, 70), c1.N, 96)[0]
+    assert np.array_equal(col, c1.d[:, 2].astype(np.float64) * (2 * c1.c[:, 70].astype(np.int64) - 1))
     ci = synth.i4g32_case(4, 64, seed=46)
     col = o.gemv_i4g32(ci.Wq, ci.scales, ci.zeros, _onehot(64, 50), ci.N, 64)[0]
     ref = (ci.s[:, 50].astype(np.float64) - ci.zeros[:, 1]) * ci.scales[:, 1].astype(np.float64)
@@ -458,6 +487,10 @@ def pin_numpy_crosscheck(o):
           * np.repeat(c2.m.reshape(c2.N, -1).astype(np.float64), 16, axis=1))
     close(o.gemv_q2_k(c2.W, c2.x, c2.N, c2.K), c2.x.astype(np.float64) @ W2.T)
 
+    c1 = synth.q1_0_case(13, 256, batch=2, seed=36)
+    W1 = c1.d.astype(np.float64).repeat(32, axis=1) * (2 * c1.c.astype(np.float64) - 1)
+    close(o.gemv_q1_0(c1.W, c1.x, c1.N, c1.K), c1.x.astype(np.float64) @ W1.T)
+
     ci = synth.i4g32_case(13, 256, batch=2, seed=26)
     Wi = ((ci.s.astype(np.float64) - np.repeat(ci.zeros.astype(np.float64), 32, axis=1))
           * np.repeat(ci.scales.astype(np.float64), 32, axis=1))
@@ -523,6 +556,12 @@ def pin_brute_force(o):
         for n in range(ci.N):
             exact_ok(yi[b, n], sum((int(ci.s[n, k]) - _F(ci.zeros[n, k // 32]))
                                    * _F(ci.scales[n, k // 32]) * _F(ci.x[b, k]) for k in range(64)))
+    c1 = synth.q1_0_case(2, 64, batch=2, seed=37)
+    y1 = o.gemv_q1_0(c1.W, c1.x, c1.N, c1.K)
+    for b in range(2):
+        for n in range(c1.N):
+            exact_ok(y1[b, n], sum(_F(c1.d[n, k // 32]) * (2 * int(c1.c[n, k]) - 1) * _F(c1.x[b, k])
+                                   for k in range(64)))
     q8 = synth.q8_0_gemv_case(2, 64, batch=1, seed=30)
     y8 = o.gemv_q8_0(q8.W, q8.x, q8.N, q8.K)
     for n in range(q8.N):
@@ -558,6 +597,6 @@ def pin_subnormal_scales(o):
 
 PINS = [pin_f16_exhaustive, pin_q4_0_worked, pin_q8_0_worked, pin_q4_k_worked,
         pin_q8_0_gemv_worked, pin_gemm_q4_worked, pin_q6_k_worked, pin_q2_k_worked,
-        pin_i4g32_worked, pin_packers_match_golden, pin_round_trip, pin_closed_forms_q4_0,
+        pin_q1_0_worked, pin_i4g32_worked, pin_packers_match_golden, pin_round_trip, pin_closed_forms_q4_0,
         pin_closed_forms_q4_k, pin_closed_forms_gemm, pin_closed_forms_new_formats,
         pin_sgemm_identity, pin_numpy_crosscheck, pin_brute_force, pin_subnormal_scales]

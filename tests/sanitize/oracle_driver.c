@@ -20,6 +20,7 @@ void lqmm_oracle_dequant_q8_0(const uint8_t *W, int64_t N, int64_t K, double *ou
 void lqmm_oracle_dequant_q4_k(const uint8_t *W, int64_t N, int64_t K, double *out);
 void lqmm_oracle_dequant_q6_k(const uint8_t *W, int64_t N, int64_t K, double *out);
 void lqmm_oracle_dequant_q2_k(const uint8_t *W, int64_t N, int64_t K, double *out);
+void lqmm_oracle_dequant_q1_0(const uint8_t *W, int64_t N, int64_t K, double *out);
 void lqmm_oracle_dequant_i4g32(const uint32_t *Wq, const float *scales, const float *zeros,
                                int64_t N, int64_t K, double *out);
 typedef void (*gemv_fn)(const uint8_t *, const float *, double *, int64_t, int64_t, int64_t,
@@ -33,6 +34,8 @@ void lqmm_oracle_gemv_q8_0(const uint8_t *, const float *, double *, int64_t, in
 void lqmm_oracle_gemv_q6_k(const uint8_t *, const float *, double *, int64_t, int64_t, int64_t,
                            const int64_t *, int64_t);
 void lqmm_oracle_gemv_q2_k(const uint8_t *, const float *, double *, int64_t, int64_t, int64_t,
+                           const int64_t *, int64_t);
+void lqmm_oracle_gemv_q1_0(const uint8_t *, const float *, double *, int64_t, int64_t, int64_t,
                            const int64_t *, int64_t);
 void lqmm_oracle_gemv_i4g32(const uint32_t *Wq, const float *scales, const float *zeros,
                             const float *x, double *y, int64_t N, int64_t K, int64_t batch,
@@ -156,6 +159,7 @@ int main(void) {
        lqmm_oracle_dequant_q4_k},
       {"q6_k", 256, 210, {208, 208}, 1, lqmm_oracle_gemv_q6_k, NULL, lqmm_oracle_dequant_q6_k},
       {"q2_k", 256, 84, {80, 82}, 2, lqmm_oracle_gemv_q2_k, NULL, lqmm_oracle_dequant_q2_k},
+      {"q1_0", 32, 6, {0, 0}, 1, lqmm_oracle_gemv_q1_0, NULL, lqmm_oracle_dequant_q1_0},
   };
   const int64_t shapes[][3] = {{1, 1, 1}, {3, 2, 2}, {7, 3, 5}};  /* N, blocks per row, batch */
   for (size_t i = 0; i < sizeof(fmts) / sizeof(fmts[0]); ++i)

@@ -29,6 +29,8 @@ MUTANTS = {
     14: "int4 codes not sign-extended",
     15: "int4 zero point added instead of subtracted",
     16: "int4 nibble order reversed within a word",
+    17: "q1_0 code bits read most significant first",
+    18: "q1_0 codes read as 0 / +d instead of -d / +d",
 }
 
 
