@@ -271,7 +271,8 @@ def build_cases(torch, only):
     next_gemv = {"q8_0": (bq.lqmm_gemv_q8_0, ["q8_0_gemv_4096x4096_b1", "q8_0_gemv_11008x4096_b1",
                                               "q8_0_gemv_12288x4096_b4"]),
                  "q6_k": (bq.lqmm_gemv_q6_k, ["q6_k_gemv_11008x4096_b1"]),
-                 "q2_k": (bq.lqmm_gemv_q2_k, ["q2_k_gemv_11008x4096_b1"])}
+                 "q2_k": (bq.lqmm_gemv_q2_k, ["q2_k_gemv_11008x4096_b1"]),
+                 "q1_0": (bq.lqmm_gemv_q1_0, ["q1_0_gemv_11008x4096_b1"])}
     for fmt, (fn, names) in next_gemv.items():
         for name in names:
             if not want(name):
@@ -835,26 +836,30 @@ def summarize_counters(pmc_dir, out_md, command):
         for cn in sorted(c):
             out.append(f"| {cn} | {c[cn]:,.0f} |\n")
         out.append("\n")
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs (its ratio to the
+        # duration is 8x the shader clock); one XCD's cycles times the 1024
+        # SIMDs (256 CUs x 4) are the SIMD-cycles of the launch.
         ratios = []
         g = c.get("GRBM_GUI_ACTIVE")
         if g:
-            ratios.append(("GRBM_GUI_ACTIVE / duration (GHz x counted instances)",
-                           g / (d * 1e3)))
+            ratios.append(("shader clock, GHz: GRBM_GUI_ACTIVE / 8 XCDs / duration",
+                           g / 8 / (d * 1e3)))
         if g and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-            ratios.append(("SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs)",
-                           c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 256)))
-        if "SQ_BUSY_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-            ratios.append(("SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES",
-                           c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_BUSY_CYCLES"]))
+            ratios.append(("matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 "
+                           "x 1024 SIMDs)", c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g / 8 * 1024)))
         for mops, peak in (("SQ_INSTS_VALU_MFMA_MOPS_F16", F16_PEAK_TFLOPS),
                            ("SQ_INSTS_VALU_MFMA_MOPS_F32", F32_PEAK_TFLOPS)):
             if c.get(mops):
-                ratios.append((f"{mops} x 512 / duration (TFLOP/s issued to the matrix cores)",
+                ratios.append((f"TFLOP/s through the matrix cores: {mops} x 512 / duration",
                                c[mops] * 512 / (d * 1e-6) / 1e12))
-                ratios.append((f"  the same against the peak ({peak:g} TFLOP/s)",
+                ratios.append((f"  the same against the {peak:g} TFLOP/s peak (2.4 GHz)",
                                c[mops] * 512 / (d * 1e-6) / 1e12 / peak))
+                if c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                    ratios.append((f"  busy cycles per 512 matrix-core flops: "
+                                   f"SQ_VALU_MFMA_BUSY_CYCLES / {mops}",
+                                   c["SQ_VALU_MFMA_BUSY_CYCLES"] / c[mops]))
         if c.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in c:
-            ratios.append(("SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+            ratios.append(("LDS bank-conflict share: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
                            c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
         if ratios:
             out.append("| ratio | value |\n|---|---:|\n")

@@ -20,11 +20,12 @@ import os
 __all__ = [
     "LqmmError", "library_path", "load",
     "lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemv_q4_0_noalloc", "lqmm_gemm_q8_0_f16",
-    "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k", "lqmm_gemv_q2_k", "lqmm_gemv_i4g32",
+    "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k", "lqmm_gemv_q2_k", "lqmm_gemv_q1_0",
+    "lqmm_gemv_i4g32",
     "lqmm_gemm_q4_0_f16", "lqmm_gemm_q4_k_f16",
     "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version",
     "Q4_0_BLOCK_BYTES", "Q8_0_BLOCK_BYTES", "Q4_K_BLOCK_BYTES", "Q6_K_BLOCK_BYTES",
-    "Q2_K_BLOCK_BYTES",
+    "Q2_K_BLOCK_BYTES", "Q1_0_BLOCK_BYTES",
 ]
 
 Q4_0_BLOCK_BYTES = 18   # 32 weights
@@ -32,6 +33,7 @@ Q8_0_BLOCK_BYTES = 34   # 32 weights
 Q4_K_BLOCK_BYTES = 144  # 256 weights
 Q6_K_BLOCK_BYTES = 210  # 256 weights
 Q2_K_BLOCK_BYTES = 84   # 256 weights
+Q1_0_BLOCK_BYTES = 6    # 32 weights
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblqmm.so")
@@ -40,7 +42,7 @@ _lib = None
 # Entry points exported by liblqmm.so (the declarations of include/lqmm.h).
 EXPORTS = ("lqmm_sgemm", "lqmm_gemv_q4_0", "lqmm_gemv_q4_0_noalloc", "lqmm_gemm_q8_0_f16",
            "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k", "lqmm_gemv_q2_k",
-           "lqmm_gemv_i4g32", "lqmm_gemm_q4_0_f16", "lqmm_gemm_q4_k_f16",
+           "lqmm_gemv_q1_0", "lqmm_gemv_i4g32", "lqmm_gemm_q4_0_f16", "lqmm_gemm_q4_k_f16",
            "lqmm_gemv_workspace_bytes", "lqmm_status_string", "lqmm_version")
 
 
@@ -69,7 +71,7 @@ def load():
     lib.lqmm_sgemm.argtypes = [p, p, p, i64, i64, i64, p]
     lib.lqmm_sgemm.restype = st
     for name in ("lqmm_gemv_q4_0", "lqmm_gemv_q4_k", "lqmm_gemv_q8_0", "lqmm_gemv_q6_k",
-                 "lqmm_gemv_q2_k"):
+                 "lqmm_gemv_q2_k", "lqmm_gemv_q1_0"):
         f = getattr(lib, name)
         f.argtypes = [p, p, p, i64, i64, i64, p, sz, p]
         f.restype = st
@@ -314,6 +316,11 @@ def lqmm_gemv_q6_k(W, x, N, out=None, workspace=None, stream=None):
 def lqmm_gemv_q2_k(W, x, N, out=None, workspace=None, stream=None):
     """y = x @ W^T with W an N x K matrix of Q2_K super-blocks (decode)."""
     return _gemv(load().lqmm_gemv_q2_k, 256, Q2_K_BLOCK_BYTES, W, x, N, out, workspace, stream)
+
+
+def lqmm_gemv_q1_0(W, x, N, out=None, workspace=None, stream=None):
+    """y = x @ W^T with W an N x K matrix of 1-bit q1_0 blocks (decode)."""
+    return _gemv(load().lqmm_gemv_q1_0, 32, Q1_0_BLOCK_BYTES, W, x, N, out, workspace, stream)
 
 
 def lqmm_gemv_i4g32(Wq, scales, zeros, x, N, out=None, workspace=None, stream=None):

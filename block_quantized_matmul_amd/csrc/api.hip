@@ -86,7 +86,7 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 bool small_only(lqmm::GemvFormat f) {
   using lqmm::GemvFormat;
   return f == GemvFormat::Q8_0 || f == GemvFormat::Q6_K || f == GemvFormat::Q2_K ||
-         f == GemvFormat::I4G32;
+         f == GemvFormat::I4G32 || f == GemvFormat::Q1_0;
 }
 
 // Bytes per row of N x K weights in format f.
@@ -100,6 +100,7 @@ int64_t gemv_row_bytes(lqmm::GemvFormat f, int64_t K) {
     case GemvFormat::Q6_K: return K / 256 * 210;
     case GemvFormat::Q2_K: return K / 256 * 84;
     case GemvFormat::I4G32: return K / 2;
+    case GemvFormat::Q1_0: return K / 32 * 6;
   }
   return 0;
 }
@@ -557,6 +558,12 @@ lqmm_status lqmm_gemv_q2_k(const void *W, const float *x, float *y, int64_t N, i
                    workspace_bytes, (hipStream_t)stream);
 }
 
+lqmm_status lqmm_gemv_q1_0(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                           int64_t batch, void *workspace, size_t workspace_bytes, void *stream) {
+  return gemv_more(lqmm::GemvFormat::Q1_0, 32, W, nullptr, nullptr, x, y, N, K, batch, workspace,
+                   workspace_bytes, (hipStream_t)stream);
+}
+
 lqmm_status lqmm_gemv_i4g32(const uint32_t *Wq, const float *scales, const float *zeros,
                             const float *x, float *y, int64_t N, int64_t K, int64_t batch,
                             void *workspace, size_t workspace_bytes, void *stream) {
@@ -610,7 +617,7 @@ size_t lqmm_gemv_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
   using lqmm::GemvFormat;
   size_t best = 0;
   for (GemvFormat f : {GemvFormat::Q4_0, GemvFormat::Q4_K, GemvFormat::Q8_0, GemvFormat::Q6_K,
-                       GemvFormat::Q2_K, GemvFormat::I4G32}) {
+                       GemvFormat::Q2_K, GemvFormat::I4G32, GemvFormat::Q1_0}) {
     const int blk = (f == GemvFormat::Q4_K || f == GemvFormat::Q6_K || f == GemvFormat::Q2_K) ? 256 : 32;
     if (K % blk != 0) continue;
     const int64_t B = small_only(f) && batch > kSmallMaxBatch ? kSmallMaxBatch : batch;

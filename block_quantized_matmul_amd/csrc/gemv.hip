@@ -1289,6 +1289,7 @@ int gemv_unit_weights(GemvFormat f) {
     case GemvFormat::Q6_K: return 128;  // FmtQ6_K: half a super-block
     case GemvFormat::Q2_K: return 128;  // FmtQ2_K: half a super-block
     case GemvFormat::I4G32: return 32;  // FmtI4G32: one group
+    case GemvFormat::Q1_0: return 32;   // FmtQ1_0: one block
   }
   return 32;
 }

@@ -1,5 +1,6 @@
-// More block formats for the dot2 GEMV (gfx950): Q8_0, the K-quants Q6_K and
-// Q2_K, and the int4 group-32 layout of the pages' int4 matmul. Each is a
+// More block formats for the dot2 GEMV (gfx950): Q8_0, the 1-bit q1_0, the
+// K-quants Q6_K and Q2_K, and the int4 group-32 layout of the pages' int4
+// matmul. Each is a
 // trait in the shape of those in gemv_common.hpp (units, staged activation
 // words, staged sums, dot2 arithmetic), so the small-problem kernel takes it
 // unchanged: "Resumo Tecnico: Llamas na Web", section "Design de Shader
@@ -98,6 +99,78 @@ struct FmtQ8_0 {
       const float d = valid ? f16_bits_to_f32(raw[r].d) : 0.0f;
 #pragma unroll
       for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, s[r][b], acc[r][b]);
+    }
+  }
+};
+
+// ---- q1_0: unit = one block (32 weights, 6 bytes) ---------------------------
+// [d fp16][32 code bits, least significant bit first] at byte 6 u (2-byte
+// aligned: a 2-byte and an unaligned 4-byte load). Word t holds weights
+// 8t..8t+7, the bits of code byte t: spread as v = b | b << 14, bit pairs
+// (0, 2), (4, 6), (1, 3), (5, 7) sit at bits 0 and 16 of v, v >> 4, v >> 1
+// and v >> 5, and one v_and_or_b32 with 0x00010001 puts each pair into the
+// mantissas of fp16 (1024.0, 1024.0): exactly (1024 + c, 1024 + c'). The
+// dot products give sum (1024 + c) x; since w = d (2c - 1),
+// sum w x = 2d (dot - 1024.5 S), so the staged sum is -1024.5 * S and the
+// scale 2d is applied in fp32.
+struct FmtQ1_0 {
+  static constexpr int kUnitWeights = 32;
+  static constexpr int kWords = 4;
+  static constexpr int kSums = 1;
+  static constexpr int kSumWords = 4;
+  static __device__ __forceinline__ int x_lo(int t) { return 8 * t; }
+  static __device__ __forceinline__ int x_hi(int t) { return 8 * t + 4; }
+  struct Raw {
+    uint32_t bits;
+    uint32_t d;
+  };
+  static __host__ __device__ __forceinline__ int64_t unit_offset(int64_t unit) { return unit * 6; }
+  static __device__ __forceinline__ Raw load(const uint8_t *row, uint32_t unit) {
+    const uint8_t *p = row + unit * 6u;
+    Raw r;
+    r.d = load_u16(p);
+    __builtin_memcpy(&r.bits, p + 2, 4);
+    return r;
+  }
+  static __device__ __forceinline__ void stage_sums(float *sums, int idx, int /*g*/, float slo,
+                                                    float shi) {
+    sums[idx] = -1024.5f * (slo + shi);
+  }
+  template <int B, int R>
+  static __device__ __forceinline__ void compute(const Raw (&raw)[R], const u32x4 *xs, int xstride,
+                                                 const float *sums, int u, int nu, bool valid,
+                                                 const UnpackMasks &k, float (&acc)[R][B]) {
+    const uint32_t pair_mask = 0x00010001u;
+    float s[R][B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float c = sums[b * nu + u];
+#pragma unroll
+      for (int r = 0; r < R; ++r) s[r][b] = c;
+    }
+#pragma unroll
+    for (int t = 0; t < kWords; ++t) {
+      u32x4 X[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) X[b] = xs[(b * kWords + t) * xstride + u];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t byte = (raw[r].bits >> (8 * t)) & 0xFFu;
+        const uint32_t v = byte | (byte << 14);
+        Nibbles n;
+        n.p0 = as_half2(and_or(v, pair_mask, k.magic));
+        n.p1 = as_half2(and_or(v >> 4, pair_mask, k.magic));
+        n.p2 = as_half2(and_or(v >> 1, pair_mask, k.magic));
+        n.p3 = as_half2(and_or(v >> 5, pair_mask, k.magic));
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[r][b] = dot_word(n, X[b], s[r][b]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float d2 = valid ? 2.0f * f16_bits_to_f32(raw[r].d) : 0.0f;
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d2, s[r][b], acc[r][b]);
     }
   }
 };

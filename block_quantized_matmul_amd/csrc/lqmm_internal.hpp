@@ -38,9 +38,9 @@ hipError_t ensure_max_lds(int bytes) {
 // ---- GEMV -------------------------------------------------------------------
 // Q4_0x2: Q4_0 weights taken two blocks (64 weights, 36 bytes) per unit, used
 // by the VALU-mode kernel when K % 64 == 0.
-// Q8_0, Q6_K, Q2_K and I4G32 (the int4 group-32 layout) run on the
-// small-problem kernel only.
-enum class GemvFormat { Q4_0, Q4_K, Q4_0x2, Q8_0, Q6_K, Q2_K, I4G32 };
+// Q8_0, Q6_K, Q2_K, I4G32 (the int4 group-32 layout) and Q1_0 (1-bit codes)
+// run on the small-problem kernel only.
+enum class GemvFormat { Q4_0, Q4_K, Q4_0x2, Q8_0, Q6_K, Q2_K, I4G32, Q1_0 };
 
 // Largest dynamic LDS one GEMV launch may use (staged activations + sums).
 constexpr int kMaxGemvLds = 144 * 1024;

@@ -51,7 +51,7 @@ GEMM_Q8 = [dict(LQMM_TUNE_GEMM_WAVES=str(w)) for w in (7, 8)]
 def _variants(kind, batch, fmt):
     if kind == "gemm":
         return GEMM_Q8 if fmt == "q8_0" else []
-    if fmt in ("q8_0", "q6_k", "q2_k", "i4g32"):  # the small-problem kernel only
+    if fmt in ("q8_0", "q6_k", "q2_k", "i4g32", "q1_0"):  # the small-problem kernel only
         return [v for v in GEMV_SMALL if v["LQMM_TUNE_GEMV_SPLITK"] != "4"]
     out = list(GEMV_SMALL) if batch <= 4 else []
     out += GEMV_VALU if batch <= 2 else []
@@ -77,10 +77,10 @@ def _setup(torch, name):
         return [t] + [t.clone() for _ in range(n - 1)]
 
     it = itertools.count()
-    if kind in ("q4_0", "q4_k", "q8_0_gemv", "q6_k", "q2_k"):
+    if kind in ("q4_0", "q4_k", "q8_0_gemv", "q6_k", "q2_k", "q1_0"):
         fmt = {"q8_0_gemv": "q8_0"}.get(kind, kind)
         fn = {"q4_0": bq.lqmm_gemv_q4_0, "q4_k": bq.lqmm_gemv_q4_k, "q8_0": bq.lqmm_gemv_q8_0,
-              "q6_k": bq.lqmm_gemv_q6_k, "q2_k": bq.lqmm_gemv_q2_k}[fmt]
+              "q6_k": bq.lqmm_gemv_q6_k, "q2_k": bq.lqmm_gemv_q2_k, "q1_0": bq.lqmm_gemv_q1_0}[fmt]
         Ws, x = rot(c.W), torch.from_numpy(c.x.copy()).to(dev)
         y = torch.empty((c.batch, c.N), dtype=torch.float32, device=dev)
         return "gemv", fmt, c.batch, lambda: fn(Ws[next(it) % len(Ws)], x, c.N, out=y), y

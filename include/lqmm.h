@@ -179,7 +179,8 @@ lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y,
  * scales applied in fp32, fp32 accumulation; every activation row on the
  * vector ALUs, in passes of up to four rows). Split-K plans, for rows longer
  * than one wave's slice (2048 weights of Q8_0 or the int4 layout, 4096 when
- * N is at least four times the CU count; 8192 of Q6_K or Q2_K), need the
+ * N is at least four times the CU count; 8192 of Q6_K or Q2_K; 2048 of
+ * q1_0, 4096 when N is at least four times the CU count), need the
  * workspace (LQMM_ERR_WORKSPACE without it).
  *   lqmm_gemv_q8_0: W is N x (K/32) Q8_0 blocks (34 bytes), K % 32 == 0.
  *   lqmm_gemv_q6_k: W is N x (K/256) Q6_K super-blocks (210 bytes), K % 256 ==
@@ -192,6 +193,11 @@ lqmm_status lqmm_gemv_q4_k(const void *W, const float *x, float *y,
  *     0. Super-block: [scales 16][qs 64][d fp16][dmin fp16]; scales[g] =
  *     sc | m << 4 for weights 16g..16g+15; w = d * sc * q - dmin * m, q =
  *     bits 2j..2j+1 of qs[32h + l] for weight k = 128h + 32j + l.
+ *   lqmm_gemv_q1_0: the 1-bit format "Llamas na Web" names under
+ *     "Extensibilidade" (q1_0; the page gives no bytes), read as the _0
+ *     family at one bit per weight: W is N x (K/32) blocks of 6 bytes,
+ *     [d fp16][4 bytes of code bits]; the bit c of weight j is bit j % 8 of
+ *     code byte j / 8; w = d * (2c - 1). K % 32 == 0.
  *   lqmm_gemv_i4g32: the int4 layout of "Compute Shaders con WebGPU para
  *     Inferencia ML", "Yendo a Cuantizado: Matmul INT4" (GPTQ/AWQ style):
  *     Wq holds N*K/8 32-bit words, weight (n, k) being nibble (n*K + k) % 8
@@ -208,6 +214,9 @@ lqmm_status lqmm_gemv_q6_k(const void *W, const float *x, float *y,
                            int64_t N, int64_t K, int64_t batch,
                            void *workspace, size_t workspace_bytes, void *stream);
 lqmm_status lqmm_gemv_q2_k(const void *W, const float *x, float *y,
+                           int64_t N, int64_t K, int64_t batch,
+                           void *workspace, size_t workspace_bytes, void *stream);
+lqmm_status lqmm_gemv_q1_0(const void *W, const float *x, float *y,
                            int64_t N, int64_t K, int64_t batch,
                            void *workspace, size_t workspace_bytes, void *stream);
 lqmm_status lqmm_gemv_i4g32(const uint32_t *Wq, const float *scales,

@@ -72,7 +72,7 @@ int main(int argc, char **argv) {
     gemv_ws_fn fn;
     int64_t blk;
   } gemvs[] = {{lqmm_gemv_q4_0, 32}, {lqmm_gemv_q4_k, 256}, {lqmm_gemv_q8_0, 32},
-               {lqmm_gemv_q6_k, 256}, {lqmm_gemv_q2_k, 256}};
+               {lqmm_gemv_q6_k, 256}, {lqmm_gemv_q2_k, 256}, {lqmm_gemv_q1_0, 32}};
   for (size_t i = 0; i < sizeof(gemvs) / sizeof(gemvs[0]); ++i) {
     gemv_ws_fn f = gemvs[i].fn;
     const int64_t K = gemvs[i].blk;
