@@ -2,16 +2,16 @@
 and of the C ABI's host code (CPU only).
 
 - The oracle (oracle/lqmm_oracle.c) is built with gcc and both sanitizers
-  together with tests/sanitize/oracle_driver.c, which calls every exported
+  together with tests/sanitize/oracle_check.c, which calls every exported
   oracle function on ragged shapes with exactly-sized buffers, with and
   without row/column subsets, with leak detection on.
 - The library's sources are built with the sanitizers on their host code
   only (device code is compiled as usual; no GPU sanitizer is involved) and
-  linked with tests/sanitize/abi_driver.c, which calls every entry point with
+  linked with tests/sanitize/abi_check.c, which calls every entry point with
   arguments the boundary must reject and checks the documented status, and,
   with no GPU visible, well-formed calls that must fail with LQMM_ERR_DEVICE.
 
-Any sanitizer report aborts the driver (-fno-sanitize-recover=all) and
+Any sanitizer report aborts the check program (-fno-sanitize-recover=all) and
 fails the test. Builds go to a temporary directory.
 """
 import os
@@ -40,10 +40,10 @@ def _run(cmd, **kw):
 def test_oracle_under_asan_ubsan(tmp_path):
     if not shutil.which("gcc"):
         pytest.skip("gcc not available")
-    exe = str(tmp_path / "oracle_driver")
+    exe = str(tmp_path / "oracle_check")
     _run(["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-fno-omit-frame-pointer",
           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
-          os.path.join(SAN, "oracle_driver.c"), os.path.join(ROOT, "oracle", "lqmm_oracle.c"),
+          os.path.join(SAN, "oracle_check.c"), os.path.join(ROOT, "oracle", "lqmm_oracle.c"),
           "-o", exe, "-lm"])
     r = _run([exe], env=ENV, timeout=300)
     assert "oracle sanitizer run: ok" in r.stdout
@@ -72,10 +72,10 @@ def test_abi_host_code_under_asan_ubsan(tmp_path):
 
     with ThreadPoolExecutor(max_workers=min(8, len(bqbuild.SOURCES))) as ex:
         objs = list(ex.map(compile_one, bqbuild.SOURCES))
-    drv = str(tmp_path / "abi_driver.o")
+    drv = str(tmp_path / "abi_check.o")
     _run([CLANG, "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
-          "-I", os.path.join(ROOT, "include"), "-c", os.path.join(SAN, "abi_driver.c"), "-o", drv])
-    exe = str(tmp_path / "abi_driver")
+          "-I", os.path.join(ROOT, "include"), "-c", os.path.join(SAN, "abi_check.c"), "-o", drv])
+    exe = str(tmp_path / "abi_check")
     _run([CLANG + "++", "-fsanitize=address,undefined", drv, *objs,
           "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
           "-o", exe])
