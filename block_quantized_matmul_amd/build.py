@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblqmm.so")
 SOURCES = ["api.hip", "gemv.hip", "gemv_small.hip", "gemv_small_more.hip", "gemm_q8_0.hip",
-           "gemm_lds.hip", "sgemm.hip"]
+           "gemm_lds.hip", "sgemm.hip", "gemv_whole.hip"]
 PROBE_LIB = os.path.join(HERE, "liblqmm_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 

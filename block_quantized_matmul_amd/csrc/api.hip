@@ -247,6 +247,7 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
   const int env_xregs = env_int("LQMM_TUNE_GEMV_XREGS");
   const int env_stream = env_int("LQMM_TUNE_GEMV_STREAM");
   const int env_stream_batch = env_int("LQMM_TUNE_GEMV_STREAM_BATCH");
+  const int env_whole = env_int("LQMM_TUNE_GEMV_WHOLE");
   const int64_t tiles = (N + 15) / 16;  // 16-row tiles of the matrix-core kernels
 
   // K-slices per tile of the coalesced kernel (one workgroup per CU): the
@@ -317,6 +318,45 @@ lqmm_status gemv_common(lqmm::GemvFormat fmt, const void *W, const float *x, flo
     if (streamed) mfma = false;
     const int bmax = mfma ? 16 : streamed ? stream_batch : 2;
     const int B = (int)(left < bmax ? left : bmax);
+    // Matrix-core kernel that requests each workgroup's whole weight share at
+    // once, when it fits (rows of at most 16 super-chunks, at most three
+    // tiles per CU, all of x in one batch of loads). By default only at one
+    // tile per CU. Measured against the coalesced kernel (cold, same
+    // process): Q4_0 4096 x 4096 batch 4 6.50 -> 5.92 us with it;
+    // 11008 and 12288 x 4096 batch 4 (three tiles per CU) 11.1 and 11.5 us
+    // against 10.4 and 10.7 us, slower. LQMM_TUNE_GEMV_WHOLE: 0 off, 1 on
+    // wherever it fits.
+    const bool whole_default = tiles <= (int64_t)num_cus;
+    if (mfma && env_whole != 0 && (env_whole == 1 || whole_default) &&
+        (fmt == GemvFormat::Q4_0 || fmt == GemvFormat::Q4_K) &&
+        K % 256 == 0 && 16 * row_bytes < ((int64_t)1 << 31)) {
+      const int64_t nsc = K / 256;
+      const int ks = 8;
+      const int cps = (int)((nsc + ks - 1) / ks);
+      const int64_t nu = K / lqmm::gemv_unit_weights(fmt);
+      const int64_t grid = tiles < num_cus ? tiles : num_cus;
+      const int64_t maxt = (tiles + grid - 1) / grid;
+      if (cps <= 2 && maxt <= 3 && (int64_t)B * nu * (fmt == GemvFormat::Q4_K ? 8 : 4) <=
+                                       lqmm::gemv_whole_max_words() &&
+          lqmm::gemv_whole_lds_bytes(fmt, cps, (int)maxt, (int)nu, B) <= (size_t)lqmm::kMaxLds) {
+        lqmm::GemvPlan pw{};
+        pw.mfma = 1;
+        pw.batch = B;
+        pw.ksplit = ks;
+        pw.cps = cps;
+        pw.depth = (int)maxt;
+        pw.grid = (int)grid;
+        pw.row_bytes = row_bytes;
+        pw.ldx = K;
+        pw.ldy = N;
+        pw.N = N;
+        hipError_t e = lqmm::gemv_whole_launch(fmt, pw, static_cast<const uint8_t *>(W),
+                                               x + b0 * K, y + b0 * N, stream);
+        if (e != hipSuccess) return LQMM_ERR_LAUNCH;
+        b0 += B;
+        continue;
+      }
+    }
     const GemvFormat f = streamed ? fs : pair_for(!mfma) ? GemvFormat::Q4_0x2 : fmt;
     const int uw = lqmm::gemv_unit_weights(f);
     const int64_t units = K / uw;

@@ -366,46 +366,6 @@ gemv_mfma_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
 // piece slots get an offset past the resource and read zeros too.
 // D chunks are in flight per wave through a ring of D register buffers.
 
-// Q4_K: unit = sub-block pair (64 weights); 4 units per super-chunk, one per
-// lane group.
-struct CoalQ4_K {
-  using F = FmtQ4_K;
-  static constexpr int kUnitsPerSC = 4;
-  static constexpr int kLaneUnits = 1;
-  // Unit j of lane group q in the super-chunk at `sc` (16-byte pieces).
-  static __device__ __forceinline__ F::Raw read(const u32x4 *sc, int q, int /*j*/) {
-    F::Raw r;
-    r.h = sc[0];
-    r.q0 = sc[1 + 2 * q];
-    r.q1 = sc[2 + 2 * q];
-    return r;
-  }
-};
-
-// Q4_0: unit = one block (32 weights, 18 bytes at byte 18 * b of the
-// super-chunk); 8 units per super-chunk, blocks 2q and 2q + 1 for lane group
-// q. Their 36 bytes start 4-byte aligned; the even block's codes start 2
-// bytes into a dword and are realigned with v_alignbyte_b32.
-struct CoalQ4_0 {
-  using F = FmtQ4_0;
-  static constexpr int kUnitsPerSC = 8;
-  static constexpr int kLaneUnits = 2;
-  static __device__ __forceinline__ F::Raw read(const u32x4 *sc, int q, int j) {
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(sc) + 9 * q;
-    F::Raw r;
-    if (j == 0) {
-      const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3], d4 = w[4];
-      r.d = d0 & 0xFFFFu;
-      r.q = u32x4{__builtin_amdgcn_alignbyte(d1, d0, 2), __builtin_amdgcn_alignbyte(d2, d1, 2),
-                  __builtin_amdgcn_alignbyte(d3, d2, 2), __builtin_amdgcn_alignbyte(d4, d3, 2)};
-    } else {
-      r.d = w[4] >> 16;
-      r.q = u32x4{w[5], w[6], w[7], w[8]};
-    }
-    return r;
-  }
-};
-
 template <class C, int U, int KS, int D>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0, int nu,

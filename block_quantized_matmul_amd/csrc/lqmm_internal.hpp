@@ -87,6 +87,18 @@ int gemv_threads();
 hipError_t gemv_launch(GemvFormat f, const GemvPlan &plan, const uint8_t *W, const float *x,
                        float *y, hipStream_t stream);
 
+// Matrix-core kernel that requests each workgroup's whole weight share at
+// once (gemv_whole.hip): Q4_0 or Q4_K rows of whole 256-weight super-chunks,
+// `ksplit` waves per 16-row tile (cps super-chunks each, ksplit * cps
+// covering the row), one tile per workgroup at a time and `depth` tiles per
+// workgroup (1..3), all of x staged (at most gemv_whole_max_words() words).
+// Uses plan fields batch, row_bytes, ldx, ldy, N, grid, ksplit, cps, depth.
+size_t gemv_whole_lds_bytes(GemvFormat f, int cps, int maxt, int nu, int nb);
+int gemv_whole_max_words();
+int gemv_whole_waves();
+hipError_t gemv_whole_launch(GemvFormat f, const GemvPlan &plan, const uint8_t *W, const float *x,
+                             float *y, hipStream_t stream);
+
 // Latency-bound kernel for small problems (gemv_small.hip): one workgroup of
 // `waves` waves per (row block, K slice); each lane takes units_per_lane
 // units of its row's slice; slices > 1 splits K across workgroups (partial

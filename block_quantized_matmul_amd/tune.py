@@ -45,6 +45,7 @@ GEMV_VALU = ([dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_STREAM="1")] +
 GEMV_MFMA = [dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_XREGS=str(xr),
                   LQMM_TUNE_GEMV_KS=str(ks), LQMM_TUNE_GEMV_DEPTH=str(d))
              for xr, ks, d in itertools.product((0, 1), (1, 2, 4, 8), (2, 4))]
+GEMV_WHOLE = [dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_WHOLE=w) for w in ("0", "1")]
 GEMM_Q8 = [dict(LQMM_TUNE_GEMM_WAVES=str(w)) for w in (7, 8)]
 
 
@@ -55,7 +56,7 @@ def _variants(kind, batch, fmt):
         return [v for v in GEMV_SMALL if v["LQMM_TUNE_GEMV_SPLITK"] != "4"]
     out = list(GEMV_SMALL) if batch <= 4 else []
     out += GEMV_VALU if batch <= 2 else []
-    out += GEMV_MFMA if batch >= 3 else []
+    out += GEMV_WHOLE + GEMV_MFMA if batch >= 3 else []
     return out
 
 
@@ -196,10 +197,10 @@ def main():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--json", default="")
     p.add_argument("--md", default="")
-    p.add_argument("--family", default="", choices=["", "small", "valu", "mfma"],
+    p.add_argument("--family", default="", choices=["", "small", "valu", "mfma", "whole"],
                    help="sweep one family of overrides only")
     args = p.parse_args()
-    fam = {"small": GEMV_SMALL, "valu": GEMV_VALU, "mfma": GEMV_MFMA}
+    fam = {"small": GEMV_SMALL, "valu": GEMV_VALU, "mfma": GEMV_MFMA, "whole": GEMV_WHOLE}
     rep = sweep(args.case, args.steps, fam.get(args.family))
     if args.json:
         with open(args.json, "w") as f:

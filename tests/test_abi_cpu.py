@@ -141,3 +141,45 @@ def test_sgemm_argument_errors(lib):
     assert f(A16, A16, A16, 4, 0, 4, None) == ERR_SHAPE
     assert f(A16, A16, A16, 4, 4, -1, None) == ERR_SHAPE
     assert f(A16, A8, A16, 4, 4, 4, None) == ERR_ALIGN
+
+
+def test_host_paths_from_many_threads(lib):
+    """Sixteen host threads at once (ctypes releases the GIL, so the calls run
+    concurrently in the library): the planner behind the workspace query
+    gives every thread the answer a single thread gets, and the argument
+    checks return their status codes. Without a GPU, well-formed calls reach
+    the per-device set-up (std::call_once) and fail with LQMM_ERR_DEVICE."""
+    import random
+    import threading
+
+    shapes = [(n, k, b) for n in (1, 100, 1024, 4096, 11008, 28672)
+              for k in (32, 256, 1024, 4096, 8192, 16384) for b in (1, 2, 4, 8, 16)]
+    expect = {s: bq.lqmm_gemv_workspace_bytes(*s) for s in shapes}
+    buf = ctypes.create_string_buffer(4096 + 16)
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    f = lib.lqmm_gemv_q4_0
+    errors = []
+    no_gpu = not os.path.exists("/dev/kfd")
+
+    def work(seed):
+        rng = random.Random(seed)
+        for _ in range(1500):
+            s = rng.choice(shapes)
+            got = bq.lqmm_gemv_workspace_bytes(*s)
+            if got != expect[s]:
+                errors.append(("workspace", s, got, expect[s]))
+            if f(None, base, base, 1, 32, 1, None, 0, None) != ERR_NULL:
+                errors.append("null")
+            if f(base, base, base, 1, 33, 1, None, 0, None) != ERR_SHAPE:
+                errors.append("shape")
+            if f(base + 4, base, base, 1, 32, 1, None, 0, None) != ERR_ALIGN:
+                errors.append("align")
+            if no_gpu and f(base, base, base, 2, 64, 1, None, 0, None) != 5:
+                errors.append("device")
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(16)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors[:5]

@@ -220,6 +220,7 @@ COAL_CASES = [("q4_k", 17, 256, 3, {}), ("q4_k", 33, 768, 8, {}), ("q4_k", 100, 
 @pytest.mark.parametrize("fmt,N,K,B,env", COAL_CASES)
 def test_coal_forms(orc, monkeypatch, xregs, fmt, N, K, B, env):
     monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
+    monkeypatch.setenv("LQMM_TUNE_GEMV_WHOLE", "0")
     monkeypatch.setenv("LQMM_TUNE_GEMV_XREGS", str(xregs))  # 1 forces it where it fits
     for k, v in env.items():
         monkeypatch.setenv(k, v)
@@ -229,6 +230,46 @@ def test_coal_forms(orc, monkeypatch, xregs, fmt, N, K, B, env):
     y = _run_q4_k(c) if fmt == "q4_k" else _run_q4_0(c)
     ref = (orc.gemv_q4_k if fmt == "q4_k" else orc.gemv_q4_0)(c.W, c.x, N, K)
     assert_close(y, ref, TOL_QUANT, f"{fmt} {N}x{K} b{B} xregs={xregs} {env}")
+
+
+# Matrix-core kernel that requests each workgroup's whole weight share at
+# once, forced through the planner's override: one to sixteen super-chunks
+# per row (a wave's second super-chunk past the row end), ragged tiles, one
+# to three tiles per CU, 3 to 16 activation rows and passes of 16 + 4.
+WHOLE_CASES = [("q4_0", 17, 256, 3), ("q4_0", 257, 2304, 4), ("q4_0", 4097, 4096, 4),
+               ("q4_0", 12288, 4096, 4), ("q4_0", 11008, 4096, 4), ("q4_0", 300, 4096, 8),
+               ("q4_0", 100, 1024, 16), ("q4_0", 65, 2048, 20),
+               ("q4_k", 33, 768, 5), ("q4_k", 4100, 4096, 4), ("q4_k", 700, 3840, 3),
+               ("q4_k", 5000, 4096, 6)]
+
+
+@pytest.mark.parametrize("fmt,N,K,B", WHOLE_CASES)
+def test_whole_share_kernel(orc, monkeypatch, fmt, N, K, B):
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
+    monkeypatch.setenv("LQMM_TUNE_GEMV_WHOLE", "1")
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(N, K, B, seed=N + K * 7 + B)
+    announce(f"{fmt} gemv whole-share kernel N={N} K={K} batch={B}")
+    y = _run_q4_k(c) if fmt == "q4_k" else _run_q4_0(c)
+    ref = (orc.gemv_q4_k if fmt == "q4_k" else orc.gemv_q4_0)(c.W, c.x, N, K)
+    assert_close(y, ref, TOL_QUANT, f"{fmt} whole {N}x{K} b{B}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_k"])
+def test_whole_share_matches_coalesced(monkeypatch, fmt):
+    """Both kernels dequantize every weight the same way and multiply the
+    same fp16 operands; only the order of the fp32 additions differs."""
+    make = synth.q4_k_case if fmt == "q4_k" else synth.q4_0_case
+    c = make(3000, 4096, 4, seed=93)
+    W, x = dev(c.W.reshape(-1)), dev(c.x)
+    call = bq.lqmm_gemv_q4_k if fmt == "q4_k" else bq.lqmm_gemv_q4_0
+    monkeypatch.setenv("LQMM_TUNE_GEMV_SMALL", "0")
+    announce(f"{fmt} whole-share kernel against the coalesced kernel")
+    out = {}
+    for whole in ("0", "1"):
+        monkeypatch.setenv("LQMM_TUNE_GEMV_WHOLE", whole)
+        out[whole] = host(call(W, x, c.N)).astype(np.float64)
+    assert np.max(np.abs(out["1"] - out["0"])) <= 1e-5 * np.abs(out["0"]).max()
 
 
 # Batch 1-2 Q4_K: the kernel that streams rows through LDS (the default at
@@ -436,22 +477,24 @@ def test_small_split_needs_workspace(monkeypatch):
 # 1e-4 * N(0,1)) or large (1e3 * N(0,1), up to ~5e3). Every batch-1/2/4
 # kernel form is forced through the planner's overrides: the streamed and
 # register-loading dot2 kernels (Q4_0 in one- and two-block units), the
-# matrix-core kernel with activations in LDS and in registers, and the
-# small-problem kernel with and without split-K.
+# matrix-core kernels (activations in LDS, in registers, and the kernel that
+# requests a workgroup's whole weight share at once), and the small-problem
+# kernel with and without split-K.
 SCALED_FORMS = [
     ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
     ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
     ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
     ("q4_0", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1", "LQMM_TUNE_GEMV_Q4_0_PAIR": "1"}),
     ("q4_0", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0", "LQMM_TUNE_GEMV_Q4_0_PAIR": "0"}),
-    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "0"}),
-    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_WHOLE": "0", "LQMM_TUNE_GEMV_XREGS": "0"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_WHOLE": "0", "LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_WHOLE": "1"}),
     ("q4_k", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1"}),
     ("q4_k", 1, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0"}),
     ("q4_k", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "1"}),
     ("q4_k", 2, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_STREAM": "0"}),
-    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "0"}),
-    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_XREGS": "1"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_WHOLE": "0", "LQMM_TUNE_GEMV_XREGS": "0"}),
+    ("q4_k", 4, {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_WHOLE": "0", "LQMM_TUNE_GEMV_XREGS": "1"}),
     ("q4_0", 1, {"LQMM_TUNE_GEMV_SMALL": "1"}),
     ("q4_0", 4, {"LQMM_TUNE_GEMV_SMALL": "1", "LQMM_TUNE_GEMV_SPLITK": "2"}),
     ("q4_k", 2, {"LQMM_TUNE_GEMV_SMALL": "1"}),
