@@ -172,15 +172,6 @@ def test_batch_rows_are_independent(orc, fmt):
         assert_close(y4[b], y1, TOL_QUANT, f"row {b} across paths")
 
 
-def test_q4_0_deterministic():
-    c = synth.make("q4_0_gemv_4096x4096_b4")
-    W, x = dev(c.W.reshape(-1)), dev(c.x)
-    announce("q4_0 determinism")
-    ys = [host(bq.lqmm_gemv_q4_0(W, x, c.N)) for _ in range(5)]
-    for y in ys[1:]:
-        assert np.array_equal(y, ys[0])
-
-
 # ----------------------------------------------------------------- Q4_K GEMV
 Q4_K_SMALL = [(1, 256, 1), (3, 512, 2), (17, 768, 8), (5, 256, 9), (9, 8704, 8),
               (70, 2048, 3), (129, 4096, 5), (2, 1280, 4), (40, 16384, 1), (257, 256, 6),
