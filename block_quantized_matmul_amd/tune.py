@@ -42,9 +42,13 @@ GEMV_VALU = ([dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_STREAM="1")] +
                    LQMM_TUNE_GEMV_R=str(r), LQMM_TUNE_GEMV_U=str(u),
                    LQMM_TUNE_GEMV_Q4_0_PAIR=str(p))
               for r, u, p in itertools.product((1, 2), (1, 2, 4), (0, 1))])
-GEMV_MFMA = [dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_XREGS=str(xr),
-                  LQMM_TUNE_GEMV_KS=str(ks), LQMM_TUNE_GEMV_DEPTH=str(d))
-             for xr, ks, d in itertools.product((0, 1), (1, 2, 4, 8), (2, 4))]
+# (activations in LDS: also one or two super-chunks per row per chunk and the
+# ring depth; activations in registers: a fixed ring)
+GEMV_MFMA = ([dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_WHOLE="0", LQMM_TUNE_GEMV_XREGS="0",
+                   LQMM_TUNE_GEMV_KS=str(ks), LQMM_TUNE_GEMV_DEPTH=str(d), LQMM_TUNE_GEMV_U=str(u))
+              for ks, d, u in itertools.product((1, 2, 4, 8), (2, 3, 4, 6), (1, 2))] +
+             [dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_WHOLE="0", LQMM_TUNE_GEMV_XREGS="1",
+                   LQMM_TUNE_GEMV_KS=str(ks)) for ks in (1, 2, 4, 8)])
 GEMV_WHOLE = [dict(LQMM_TUNE_GEMV_SMALL="0", LQMM_TUNE_GEMV_WHOLE=w) for w in ("0", "1")]
 GEMM_Q8 = [dict(LQMM_TUNE_GEMM_WAVES=str(w)) for w in (7, 8)]
 
