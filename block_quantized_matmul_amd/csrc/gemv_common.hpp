@@ -220,16 +220,22 @@ struct FmtQ4_K {
     return t < 4 ? r.q0[t & 3] : r.q1[t & 3];
   }
 
-  // 6-bit scale and min of sub-block s from the scale words h.y, h.z, h.w.
-  static __device__ __forceinline__ void scale_min(const u32x4 &h, int s, uint32_t &sc,
-                                                   uint32_t &m) {
-    uint32_t sh = (s & 3) * 8;
-    uint32_t b1 = (h.y >> sh) & 0xFF, b2 = (h.z >> sh) & 0xFF, b3 = (h.w >> sh) & 0xFF;
-    uint32_t sc_lo = b1 & 63, m_lo = b2 & 63;
-    uint32_t sc_hi = (b3 & 15) | ((b1 >> 6) << 4);
-    uint32_t m_hi = (b3 >> 4) | ((b2 >> 6) << 4);
-    sc = s < 4 ? sc_lo : sc_hi;
-    m = s < 4 ? m_lo : m_hi;
+  // 6-bit scales and mins of sub-blocks 2 * pair and 2 * pair + 1 from the
+  // scale words h.y, h.z, h.w, as 16-bit lanes (sub-block 2 * pair low).
+  // Their fields are bytes j and j + 1 (j = 2 * (pair & 1)) of the three
+  // words: 6-bit fields of words 1 and 2 for sub-blocks 0..3, 4 + 2 bits of
+  // word 3 and of word 1 (scale) or 2 (min) for 4..7. One byte permute per
+  // word moves both bytes to the low byte of a 16-bit lane.
+  static __device__ __forceinline__ void scale_min_pair(const u32x4 &h, int pair, uint32_t &sc,
+                                                        uint32_t &m) {
+    const uint32_t sel = 0x0C010C00u + (uint32_t)(pair & 1) * 0x00020002u;
+    const uint32_t b1 = __builtin_amdgcn_perm(h.y, h.y, sel);
+    const uint32_t b2 = __builtin_amdgcn_perm(h.z, h.z, sel);
+    const uint32_t b3 = __builtin_amdgcn_perm(h.w, h.w, sel);
+    const uint32_t sc_hi = (b3 & 0x000F000Fu) | ((b1 >> 2) & 0x00300030u);
+    const uint32_t m_hi = ((b3 >> 4) & 0x000F000Fu) | ((b2 >> 2) & 0x00300030u);
+    sc = pair < 2 ? b1 & 0x003F003Fu : sc_hi;
+    m = pair < 2 ? b2 & 0x003F003Fu : m_hi;
   }
 
   // Unit uc of a chunk of whole super-blocks copied to LDS at `slot`.
@@ -299,9 +305,9 @@ struct FmtQ4_K {
     for (int r = 0; r < R; ++r) {
       float d = valid ? f16_bits_to_f32(raw[r].h.x & 0xFFFF) : 0.0f;
       float dmin = valid ? f16_bits_to_f32(raw[r].h.x >> 16) : 0.0f;
-      uint32_t sc0, m0, sc1, m1;
-      scale_min(raw[r].h, 2 * pair, sc0, m0);
-      scale_min(raw[r].h, 2 * pair + 1, sc1, m1);
+      uint32_t sc, m;
+      scale_min_pair(raw[r].h, pair, sc, m);
+      const uint32_t sc0 = sc & 0xFF, sc1 = sc >> 16, m0 = m & 0xFF, m1 = m >> 16;
       float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1;
       // -dmin*m*S = dmin*m*(-1024*S)/1024 (lo) = dmin*m*(-64*S)/64 (hi).
       float dm0 = dmin * (float)m0 * (1.0f / 1024.0f);
