@@ -795,8 +795,8 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
 // DR chunks are in flight during the arithmetic. (Reading the next chunk's
 // unit during the current chunk's arithmetic hid that LDS read but had the
 // wave wait for the next chunk before computing the current one, with one
-// chunk in flight meanwhile: Q4_K 28672 x 8192 batch 1 27.2-27.7 us against
-// 25.8 us, batch 2 32.0-32.2 against 30.9 us, same process.)
+// chunk in flight meanwhile: Q4_K 28672 x 8192 batch 1 26.0 us against
+// 25.1 us, batch 2 31.7 against 30.9 us, same process.)
 // Waits: as in gemv_coalr_kernel (loads return in order; a slot is refilled
 // only after the wave's reads of it are complete; chunks past the wave's
 // work come from an empty buffer range).
