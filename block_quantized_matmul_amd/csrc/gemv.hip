@@ -843,8 +843,13 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   uint8_t *const ring = smem + stream_stage_bytes<F>(B, nu) + (size_t)wave * DR * kStreamSlot;
   const int64_t nwaves = (int64_t)gridDim.x * kStreamWaves;
-  const int64_t wave_id = (int64_t)blockIdx.x * kStreamWaves + wave;
-  const int64_t n_rows = wave_id < N ? (N - wave_id + nwaves - 1) / nwaves : 0;
+  // Row bookkeeping in 32 bits (N <= 2^31, so every row index and count
+  // below stays under 2^32): wave-uniform, so it runs on the scalar unit
+  // (64-bit signed compares have no scalar form and took vector
+  // instructions in the chunk loop).
+  const uint32_t nw32 = (uint32_t)nwaves, n32 = (uint32_t)N;
+  const uint32_t wave_id = blockIdx.x * (uint32_t)kStreamWaves + (uint32_t)wave;
+  const uint32_t n_rows = wave_id < n32 ? (n32 - wave_id + nw32 - 1) / nw32 : 0u;
   // Chunks per row: Q4_K 1 or 2, kept a run-time value, so that the chunk
   // loop below stays a loop (the compiler keeps it within 128 VGPRs); the
   // Q4_0 pair form takes one chunk per row (with a second one it spilled).
@@ -856,12 +861,12 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
   };
 
   // Request item `issued` (chunk ic of row irow) into ring slot `slot`.
-  int64_t irow = wave_id, issued = 0;
+  uint32_t irow = wave_id, issued = 0;
   int ic = 0;
   auto issue = [&](int slot) {
-    const bool live = issued < n_rows * cpr;
-    const int64_t r = irow < N ? irow : N - 1;
-    const rsrc_t rs = make_rsrc(W + r * row_bytes + (int64_t)ic * kStreamChunk,
+    const bool live = issued < n_rows * (uint32_t)cpr;
+    const uint32_t r = irow < n32 ? irow : n32 - 1;
+    const rsrc_t rs = make_rsrc(W + (int64_t)r * row_bytes + (int64_t)ic * kStreamChunk,
                                 live ? (uint32_t)(chunk_units(ic) * kStreamUnitBytes) : 0u);
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
@@ -872,7 +877,7 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
     ++issued;
     if (++ic == cpr) {
       ic = 0;
-      irow += nwaves;
+      irow += nw32;
     }
   };
   // Stage the activation words and the per-(b, u) sums of gemv_kernel; at
@@ -969,8 +974,8 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
 
   const UnpackMasks kmask;
   int slot = 0;
-  int64_t crow = wave_id;
-  for (int64_t rr = 0; rr < n_rows; ++rr) {
+  uint32_t crow = wave_id;
+  for (uint32_t rr = 0; rr < n_rows; ++rr) {
     float acc[1][B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[0][b] = 0.0f;
@@ -999,9 +1004,9 @@ gemv_stream_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nu,
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const float v = group_sum(acc[0][b], kWave);
-      if (lane == kWave - 1) y[b * ldy + crow] = v;
+      if (lane == kWave - 1) y[b * ldy + (int64_t)crow] = v;
     }
-    crow += nwaves;
+    crow += nw32;
   }
   // no buffer-to-LDS load may be left in flight when the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
