@@ -425,6 +425,9 @@ def pin_sgemm_identity(o):
     E[2, 4] = 1
     C = o.sgemm(E, B)
     assert np.array_equal(C[2], B[4].astype(np.float64)) and not C[[0, 1, 3, 4, 5, 6]].any()
+    # a row subset (any order) gives those rows of A * I = A
+    rows = [6, 0, 3]
+    assert np.array_equal(o.sgemm(A, I5, rows=rows), A[rows].astype(np.float64))
 
 
 # ------------------------------------------------------ library-routine pins
