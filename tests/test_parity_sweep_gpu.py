@@ -6,6 +6,9 @@ CPU oracle on the same inputs. The shapes are drawn once from a fixed seed
 activation rows), so that tails, split-K plans and batch passes are reached
 at sizes no hand-picked case names.
 
+The further block formats (Q8_0, Q6_K, Q2_K, q1_0 and the int4 group-32
+layout) run through their decode GEMVs the same way.
+
 Outputs of more than 256 elements take the usual bars (2e-3 for the
 quantized paths, 1e-5 / 1e-4 for fp32). Smaller outputs are checked per
 element against a rounding bound, since one dot product can cancel by a large
@@ -72,8 +75,22 @@ def _gemm_draws():
     return out
 
 
+def _format_draws():
+    rng = np.random.default_rng(20243)
+    out = []
+    for i in range(15):
+        fmt = ("q8_0", "q6_k", "q2_k", "q1_0", "i4g32")[i % 5]
+        blk = 256 if fmt in ("q6_k", "q2_k") else 32
+        K = blk * int(rng.integers(1, 16384 // blk + 1))
+        B = int(rng.choice([1, 1, 2, 3, 4, 5, 9]))
+        N = _log_uniform(rng, max(1, min(20000, int(MAX_MACS // (K * B)))))
+        out.append((fmt, N, K, B))
+    return out
+
+
 GEMV_DRAWS = _gemv_draws()
 GEMM_DRAWS = _gemm_draws()
+FORMAT_DRAWS = _format_draws()
 
 
 def _ids(draws):
@@ -131,3 +148,29 @@ def test_gemm_random_shapes(orc, fmt, M, N, K):
     w = getattr(orc, f"dequant_{fmt}")(c.W, N, K)
     bound = 2.0 ** -9 * (np.abs(c.X.astype(np.float64)) @ np.abs(w).T)
     assert np.all(np.abs(Y - ref) <= bound + 2.0 ** -10 * np.abs(ref))
+
+
+FORMAT_MAKE = {"q8_0": synth.q8_0_gemv_case, "q6_k": synth.q6_k_case, "q2_k": synth.q2_k_case,
+               "q1_0": synth.q1_0_case, "i4g32": synth.i4g32_case}
+
+
+@pytest.mark.parametrize("fmt,N,K,B", FORMAT_DRAWS, ids=_ids(FORMAT_DRAWS))
+def test_format_gemv_random_shapes(orc, fmt, N, K, B):
+    c = FORMAT_MAKE[fmt](N, K, B, seed=N * 13 + K + B)
+    announce(f"sweep {fmt} gemv N={N} K={K} batch={B}")
+    if fmt == "i4g32":
+        y = bq.lqmm_gemv_i4g32(dev(c.Wq.view(np.int32)), dev(c.scales), dev(c.zeros), dev(c.x), N)
+        ref = orc.gemv_i4g32(c.Wq, c.scales, c.zeros, c.x, N, K)
+    else:
+        y = getattr(bq, f"lqmm_gemv_{fmt}")(dev(c.W.reshape(-1)), dev(c.x), N)
+        ref = getattr(orc, f"gemv_{fmt}")(c.W, c.x, N, K)
+    y = host(y).astype(np.float64)
+    assert np.isfinite(y).all()
+    if N * B > 256:
+        assert_close(y, ref, TOL_QUANT, f"{fmt} {N}x{K} b{B}")
+        return
+    w = (orc.dequant_i4g32(c.Wq, c.scales, c.zeros, N, K) if fmt == "i4g32"
+         else getattr(orc, f"dequant_{fmt}")(c.W, N, K))
+    bound = (2.0 ** -11 + 2.0 ** -9) * (np.abs(c.x.astype(np.float64)) @ np.abs(w).T)
+    assert np.all(np.abs(y - ref) <= bound + 2.0 ** -24 * np.abs(ref)), \
+        float(np.max(np.abs(y - ref) / (bound + 1e-300)))
