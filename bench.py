@@ -97,6 +97,9 @@ def parse():
     p.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "BENCH_LOG", "OUT_MD", "COMMAND"),
                    help="host only: write a markdown summary of a rocprofv3 kernel trace of "
                         "this benchmark (timed launches per case apart from the others)")
+    p.add_argument("--summarize-series", nargs=4,
+                   metavar=("TRACE_DIR", "BENCH_LOG", "OUT_MD", "COMMAND"),
+                   help="write a markdown summary of the timed launches' durations in order")
     p.add_argument("--summarize-traffic", nargs=3, metavar=("PMC_DIR", "CALIB_MIB", "COMMAND"),
                    help="host only: write the GEMV cases' HBM traffic summary from rocprofv3 "
                         "--pmc runs under PMC_DIR/<case>.fetch and PMC_DIR/<case>.write")
@@ -753,6 +756,59 @@ def _counter_per_dispatch(csv_path, counter):
     return per
 
 
+def summarize_series(trace_dir, bench_log, out_md, command):
+    """Markdown summary of how each case's launch durations evolve over its
+    timed graph (launches in order, means of consecutive blocks of ten),
+    next to the same kernel's launches in the settle and warmup replays
+    before the timed region. Launches are identified as in summarize_trace."""
+    import csv
+    line = None
+    for l in open(bench_log):
+        l = l.strip()
+        if l.startswith("{") and '"metric"' in l:
+            line = json.loads(l)
+    if line is None:
+        raise SystemExit(f"no JSON line in {bench_log}")
+    order = list(line["cases"].keys())
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    b = max(i for i, n in enumerate(names) if "timed_region_begin_marker" in n)
+    e = min(i for i, n in enumerate(names) if "timed_region_end_marker" in n and i > b)
+    timed = rows[b + 1:e]
+    per = len(timed) // len(order)
+    if per * len(order) != len(timed) or per == 0:
+        raise SystemExit(f"{len(timed)} timed launches do not split over {len(order)} cases")
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+    out = [f"# Launch durations over the timed graphs: {', '.join(order)}\n\n",
+           "Command, from the repository root on one MI355X after "
+           "`cd /tmp && export TMPDIR=/tmp` (paths relative to the repository):\n\n",
+           f"```\n{command}\n```\n\n",
+           f"Each case's {per} timed launches run back to back in one HIP graph, the cases "
+           "one after another in the order listed. Durations are kernel start to end from "
+           "the trace, in us.\n\n",
+           "| case | kernel | min | median | max | settle and warmup launches: count, median |\n"
+           "|---|---|---:|---:|---:|---:|\n"]
+    series = []
+    for ci, case in enumerate(order):
+        rs = timed[ci * per:(ci + 1) * per]
+        kn = sorted(set(r["Kernel_Name"] for r in rs))
+        d = [dur(r) for r in rs]
+        pre = sorted(dur(r) for r in rows[:b] if r["Kernel_Name"] in kn)
+        pre_s = f"{len(pre)}, {_pct(pre, 50):.2f}" if pre else "-"
+        ds = sorted(d)
+        out.append(f"| {case} | `{' + '.join(_short_kernel(k) for k in kn)}` | {ds[0]:.2f} | "
+                   f"{_pct(ds, 50):.2f} | {ds[-1]:.2f} | {pre_s} |\n")
+        blocks = [sum(d[i:i + 10]) / len(d[i:i + 10]) for i in range(0, len(d), 10)]
+        series.append((case, blocks))
+    out.append("\nMeans of consecutive blocks of ten timed launches, in launch order:\n\n")
+    for case, blocks in series:
+        out.append(f"- {case}: " + ", ".join(f"{v:.1f}" for v in blocks) + "\n")
+    with open(out_md, "w") as f:
+        f.write("".join(out))
+    print(f"wrote {out_md}")
+
+
 def summarize_traffic(pmc_dir, calib_mib, command):
     """HBM bytes per launch of every GEMV case, from one FETCH_SIZE run and
     one WRITE_SIZE run per case (PMC_DIR/<case>.fetch, PMC_DIR/<case>.write;
@@ -875,6 +931,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_series:
+        summarize_series(*args.summarize_series)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
