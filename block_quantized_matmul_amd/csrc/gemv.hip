@@ -421,9 +421,10 @@ gemv_coal_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit0
   // Chunk c of tile g (clamped to the last tile) into dst.
   auto load = [&](u32x4 (&dst)[NI], int g, int c) {
     const int gc = g < ngroups ? g : ngroups - 1;
-    const int64_t r0 = (int64_t)gc * 16;
-    const int64_t rows = N - r0 < 16 ? N - r0 : 16;
-    const rsrc_t rs = make_rsrc(W + r0 * row_bytes + unit0_bytes,
+    // 32-bit, wave-uniform (gc < ceil(N / 16), N <= 2^31): scalar compares
+    const uint32_t r0 = (uint32_t)gc * 16u, left = (uint32_t)N - r0;
+    const int64_t rows = left < 16u ? left : 16u;
+    const rsrc_t rs = make_rsrc(W + (int64_t)r0 * row_bytes + unit0_bytes,
                                 (uint32_t)(rows * row_bytes - unit0_bytes));
     const int soff = chunk_start(c) / C::kUnitsPerSC * 144;
 #pragma unroll
@@ -630,9 +631,10 @@ gemv_coalr_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int64_t unit
   auto issue = [&](int slot) {
     const bool live = issued < n_items;
     const int gc = ig < ngroups ? ig : ngroups - 1;
-    const int64_t r0 = (int64_t)gc * 16;
-    const int64_t rows = N - r0 < 16 ? N - r0 : 16;
-    const rsrc_t rs = make_rsrc(W + r0 * row_bytes + unit0_bytes,
+    // 32-bit, wave-uniform (gc < ceil(N / 16), N <= 2^31): scalar compares
+    const uint32_t r0 = (uint32_t)gc * 16u, left = (uint32_t)N - r0;
+    const int64_t rows = left < 16u ? left : 16u;
+    const rsrc_t rs = make_rsrc(W + (int64_t)r0 * row_bytes + unit0_bytes,
                                 live ? (uint32_t)(rows * row_bytes - unit0_bytes) : 0u);
     const int sc = sc0 + ic < nsc ? sc0 + ic : nsc - 1;
 #pragma unroll

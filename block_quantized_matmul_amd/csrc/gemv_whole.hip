@@ -111,12 +111,13 @@ gemv_whole_kernel(const uint8_t *__restrict__ W, int64_t row_bytes, int nsc,
     for (int it = 0; it < MAXT; ++it) {
       const int g = g0 + it * group_stride;
       const int gc = g < ngroups ? g : ngroups - 1;
-      const int64_t r0 = (int64_t)gc * 16;
-      const int64_t rows = N - r0 < 16 ? N - r0 : 16;
+      // 32-bit, wave-uniform (gc < ceil(N / 16), N <= 2^31): scalar compares
+      const uint32_t r0 = (uint32_t)gc * 16u, left = (uint32_t)N - r0;
+      const int64_t rows = left < 16u ? left : 16u;
 #pragma unroll
       for (int c = 0; c < CPS; ++c) {
         const bool live = g < ngroups && sc0 + c < nsc;
-        const rsrc_t rs = make_rsrc(W + r0 * row_bytes, live ? (uint32_t)(rows * row_bytes) : 0u);
+        const rsrc_t rs = make_rsrc(W + (int64_t)r0 * row_bytes, live ? (uint32_t)(rows * row_bytes) : 0u);
         const int sc = sc0 + c < nsc ? sc0 + c : nsc - 1;
         uint8_t *dst = slots + (it * CPS + c) * kWholeChunk;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)off[0], sc * 144, 0, 0);
