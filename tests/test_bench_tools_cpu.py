@@ -1,6 +1,7 @@
 """Host logic of the benchmark: the refusal of more than one GPU, and the
-summaries of rocprofv3 kernel traces that the committed profiles are made
-with, on a small synthetic trace whose statistics are known."""
+summaries of rocprofv3 kernel traces and counter runs that the committed
+profiles (and the bench line's `traffic`) are made with, on small synthetic
+inputs whose statistics are known."""
 import csv
 import json
 import os
@@ -109,3 +110,45 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU only" in r.stdout + r.stderr
+
+
+def _pmc(d, rows):
+    d.mkdir(parents=True)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summarize_traffic_scaling(tmp_path, monkeypatch):
+    """FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by what it
+    reads for the calibration copy of 256 MiB: here FETCH_SIZE counts half
+    the bytes (scale 2) and WRITE_SIZE all of them (scale 1)."""
+    kern = "void lqmm::(anonymous namespace)::kern_a<1, 2>(int const*, int)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, neg_kernel_cuda>(int)"
+    pmc = tmp_path / "pmc"
+    fetch, write = [], []
+    for i, (fv, wv) in enumerate([(1000.0, 10.0), (1002.0, 10.0), (998.0, 10.0)]):
+        # a counter is summed over the rows of one dispatch (one per XCD here: two halves)
+        fetch += [dict(Dispatch_Id=i, Kernel_Name=kern, Counter_Name="FETCH_SIZE",
+                       Counter_Value=fv / 2)] * 2
+        write += [dict(Dispatch_Id=i, Kernel_Name=kern, Counter_Name="WRITE_SIZE",
+                       Counter_Value=wv)]
+    fetch.append(dict(Dispatch_Id=9, Kernel_Name=neg, Counter_Name="FETCH_SIZE",
+                      Counter_Value=256 * 1024 / 2))
+    write.append(dict(Dispatch_Id=9, Kernel_Name=neg, Counter_Name="WRITE_SIZE",
+                      Counter_Value=256 * 1024))
+    _pmc(pmc / "case_a.fetch" / "host", fetch)
+    _pmc(pmc / "case_a.write" / "host", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    bench.summarize_traffic(str(pmc), 256, "CMD")
+    t = json.loads(out.read_text())
+    c = t["cases"]["case_a"]
+    assert c["fetch_scale"] == 2.0 and c["write_scale"] == 1.0
+    assert c["dispatches"] == {"fetch": 3, "write": 3}
+    assert c["fetch_kib_per_dispatch"] == 1000.0 and c["write_kib_per_dispatch"] == 10.0
+    assert c["hbm_bytes_per_launch"] == (1000 * 2 + 10) * 1024
+    assert t["kernel_source_sha256"] == bench.kernel_source_sha256()
+    assert t["command"] == "CMD"
