@@ -174,3 +174,65 @@ def test_format_gemv_random_shapes(orc, fmt, N, K, B):
     bound = (2.0 ** -11 + 2.0 ** -9) * (np.abs(c.x.astype(np.float64)) @ np.abs(w).T)
     assert np.all(np.abs(y - ref) <= bound + 2.0 ** -24 * np.abs(ref)), \
         float(np.max(np.abs(y - ref) / (bound + 1e-300)))
+
+
+# Every kernel family forced through the planner's tuning overrides on random
+# shapes (the planner falls back where a forced form does not fit the shape):
+# the matrix-core kernels at any batch, with activations in registers or in
+# LDS, the whole-share kernel and the MFMA-layout kernel; the vector-ALU
+# kernels (register-loading and streamed) at any batch.
+FORCED = {
+    "mfma": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "1"},
+    "mfma_xregs": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "1",
+                   "LQMM_TUNE_GEMV_WHOLE": "0", "LQMM_TUNE_GEMV_XREGS": "1"},
+    "mfma_lds": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "1",
+                 "LQMM_TUNE_GEMV_WHOLE": "0", "LQMM_TUNE_GEMV_XREGS": "0"},
+    "mfma_whole": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "1",
+                   "LQMM_TUNE_GEMV_WHOLE": "1"},
+    "mfma_layout": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "1",
+                    "LQMM_TUNE_GEMV_LDSK": "0"},
+    "valu_regs": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "0",
+                  "LQMM_TUNE_GEMV_STREAM": "0"},
+    "valu_stream": {"LQMM_TUNE_GEMV_SMALL": "0", "LQMM_TUNE_GEMV_MFMA": "0",
+                    "LQMM_TUNE_GEMV_STREAM": "1"},
+}
+
+
+def _forced_draws():
+    rng = np.random.default_rng(20244)
+    out = []
+    for i in range(16):
+        fmt = "q4_0" if i % 2 == 0 else "q4_k"
+        blk = 32 if fmt == "q4_0" else 256
+        K = blk * int(rng.integers(1, 16384 // blk + 1))
+        B = int(rng.choice([1, 2, 3, 4, 7, 8, 16]))
+        N = _log_uniform(rng, max(1, min(5000, int(MAX_MACS // (K * B)))))
+        out.append((fmt, N, K, B))
+    return out
+
+
+FORCED_DRAWS = _forced_draws()
+
+
+@pytest.mark.parametrize("form", sorted(FORCED))
+@pytest.mark.parametrize("fmt,N,K,B", FORCED_DRAWS, ids=_ids(FORCED_DRAWS))
+def test_gemv_forced_forms_random_shapes(orc, monkeypatch, form, fmt, N, K, B):
+    for k, v in FORCED[form].items():
+        monkeypatch.setenv(k, v)
+    make = synth.q4_0_case if fmt == "q4_0" else synth.q4_k_case
+    c = make(N, K, B, seed=N * 17 + K * 5 + B)
+    announce(f"sweep {fmt} gemv N={N} K={K} batch={B} forced={form}")
+    fn = bq.lqmm_gemv_q4_0 if fmt == "q4_0" else bq.lqmm_gemv_q4_k
+    try:
+        y = host(fn(dev(c.W.reshape(-1)), dev(c.x), N)).astype(np.float64)
+    except bq.LqmmError as e:  # an override the planner cannot honour for this shape
+        pytest.skip(f"refused: {e}")
+    ref = getattr(orc, f"gemv_{fmt}")(c.W, c.x, N, K)
+    assert np.isfinite(y).all()
+    if N * B > 256:
+        assert_close(y, ref, TOL_QUANT, f"{fmt} {N}x{K} b{B} {form}")
+        return
+    w = getattr(orc, f"dequant_{fmt}")(c.W, N, K)
+    bound = (2.0 ** -11 + 2.0 ** -9) * (np.abs(c.x.astype(np.float64)) @ np.abs(w).T)
+    assert np.all(np.abs(y - ref) <= bound + 2.0 ** -24 * np.abs(ref)), \
+        float(np.max(np.abs(y - ref) / (bound + 1e-300)))
